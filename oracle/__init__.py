@@ -1,0 +1,175 @@
+"""CPU oracle of the Mamba-1 S6 selective scan (fp64, sequential token loop).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may call this package; the product path
+(the HIP library and its binding) never imports it, and it imports nothing
+from there.
+
+The arithmetic lives in ``ss_oracle.c`` (plain C, IEEE double, libm); this
+module only marshals numpy arrays into it and splits independent (batch,
+channel) rows over threads (ctypes releases the GIL during each call). Rows
+never interact, so the split changes no result: every row's token loop stays
+sequential in one call.
+
+Every function here is pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ss_oracle.c")
+_LIB = os.path.join(_HERE, "libssoracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ss_oracle.c with gcc (no fast-math) into libssoracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [ctypes.c_int] + [dp] * 3 + [i64, i64]
+        lib.oracle_update.restype = ctypes.c_int
+        lib.oracle_update.argtypes = [i64, i64, i64] + [dp] * 9 + [ctypes.c_int, dp, i64, i64]
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _threads(threads: Optional[int]) -> int:
+    if threads is not None:
+        return max(1, int(threads))
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _split_rows(rows: int, parts: int):
+    parts = max(1, min(parts, rows))
+    edges = [rows * k // parts for k in range(parts + 1)]
+    return [(edges[k], edges[k + 1]) for k in range(parts) if edges[k + 1] > edges[k]]
+
+
+def softplus(v: float) -> float:
+    return _load().oracle_softplus(float(v))
+
+
+def scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=None, dt_softplus=True,
+         return_states=False, threads=None):
+    """Prompt scan. x, dt, z: [batch, channels, L]; B, C: [batch, N, L];
+    A: [channels, N]; D, dt_bias: [channels]; h0: [batch, channels, N];
+    reset: [batch, L] (nonzero = first token of a document).
+
+    Returns (y [batch, channels, L], h_last [batch, channels, N]) in float64,
+    plus states [batch, channels, L, N] when return_states is set.
+    """
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("x must be [batch, channels, seq]")
+    batch, channels, L = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    dt = _f64(dt, x.shape)
+    A = _f64(A, (channels, N))
+    B = _f64(B, (batch, N, L))
+    C = _f64(C, (batch, N, L))
+    D = _f64(D, (channels,))
+    z = _f64(z, x.shape)
+    dt_bias = _f64(dt_bias, (channels,))
+    h0 = _f64(h0, (batch, channels, N))
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset) != 0, dtype=np.uint8)
+        if reset.shape != (batch, L):
+            raise ValueError("reset must be [batch, seq]")
+    y = np.empty((batch, channels, L), dtype=np.float64)
+    h_last = np.empty((batch, channels, N), dtype=np.float64)
+    states = np.empty((batch, channels, L, N), dtype=np.float64) if return_states else None
+    lib = _load()
+
+    def run(rb_re):
+        rc = lib.oracle_scan(batch, channels, N, L, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(reset), int(bool(dt_softplus)),
+                             _ptr(y), _ptr(h_last), _ptr(states), rb_re[0], rb_re[1])
+        if rc != 0:
+            raise ValueError("oracle_scan rejected its arguments")
+
+    parts = _split_rows(batch * channels, _threads(threads))
+    if len(parts) <= 1:
+        for p in parts:
+            run(p)
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    if return_states:
+        return y, h_last, states
+    return y, h_last
+
+
+def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, threads=None):
+    """Decode step. state: [batch, channels, N] (not modified; the updated
+    state is returned); x, dt, z: [batch, channels]; B, C: [batch, N].
+
+    Returns (y [batch, channels], new_state [batch, channels, N]) in float64.
+    """
+    new_state = np.array(_f64(state), dtype=np.float64, copy=True)
+    if new_state.ndim != 3:
+        raise ValueError("state must be [batch, channels, state_dim]")
+    batch, channels, N = new_state.shape
+    x = _f64(x, (batch, channels))
+    dt = _f64(dt, (batch, channels))
+    A = _f64(A, (channels, N))
+    B = _f64(B, (batch, N))
+    C = _f64(C, (batch, N))
+    D = _f64(D, (channels,))
+    z = _f64(z, (batch, channels))
+    dt_bias = _f64(dt_bias, (channels,))
+    y = np.empty((batch, channels), dtype=np.float64)
+    lib = _load()
+
+    def run(rb_re):
+        rc = lib.oracle_update(batch, channels, N, _ptr(new_state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
+                               rb_re[0], rb_re[1])
+        if rc != 0:
+            raise ValueError("oracle_update rejected its arguments")
+
+    parts = _split_rows(batch * channels, _threads(threads))
+    if len(parts) <= 1:
+        for p in parts:
+            run(p)
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return y, new_state

@@ -1,0 +1,139 @@
+/*
+ * ss_oracle.c -- CPU reference of the Mamba-1 S6 selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously correct oracle
+ * the HIP path is checked against. Only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the product path never does.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * Arithmetic is IEEE double with libm exp/log1p; build without fast-math.
+ * Every (batch, channel) row is an independent sequential token loop.
+ *
+ * What is computed (nnterp "selective_scan" page, class docstring: the
+ * per-channel recurrence and the step size; TransformerLens "ssm_mixer" page,
+ * compute_ssm_state: the same recurrence written per state coordinate):
+ *
+ *   dt_t = softplus(dt_raw_t + dt_bias)           (or dt_raw_t + dt_bias)
+ *   h_t  = exp(dt_t * A) * h_{t-1} + dt_t * B_t * x_t
+ *   y_t  = (C_t . h_t + D * x_t) * silu(z_t)       (gate optional)
+ *
+ * Readings where the pages leave a step open:
+ *  - B is discretised as dt * B (both pages print it that way).
+ *  - y_t reads the updated state h_t.
+ *  - The gate multiplies the whole pre-gate output, D * x included (the
+ *    ssm_mixer page calls y before the gate "the pre-gate scan output" and
+ *    includes D * x in it).
+ *  - A prompt without an initial state starts from zeros.
+ *  - Hard reset ("s6_reset" post, Enforced Boundary Resetting, in the
+ *    convention "the state is zeroed before a document's first token"):
+ *    reset_t != 0 makes the decay of that token zero, so h_t = dt_t*B_t*x_t.
+ *  - The decode step is the same body for one token, the state read and
+ *    written in place, y from the updated state.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* softplus(v) = log(1 + e^v), written in the form that does not overflow. */
+double oracle_softplus(double v) {
+    return fmax(v, 0.0) + log1p(exp(-fabs(v)));
+}
+
+/* silu(z) = z * sigmoid(z) */
+static double silu(double z) {
+    return z / (1.0 + exp(-z));
+}
+
+/* Step size of one token of one channel. */
+static double step_size(double dt_raw, const double* dt_bias, int64_t c, int dt_softplus) {
+    double v = dt_raw + (dt_bias ? dt_bias[c] : 0.0);
+    return dt_softplus ? oracle_softplus(v) : v;
+}
+
+/*
+ * One token of one channel: update h[0..N) in place and return y before the
+ * gate. Bt, Ct point at state coordinate 0 of this token; consecutive state
+ * coordinates are bc_stride elements apart.
+ */
+static double s6_token(int64_t N, double* h, double d, double xv, const double* A_row,
+                       const double* Bt, const double* Ct, int64_t bc_stride, int reset) {
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double a = reset ? 0.0 : exp(d * A_row[n]);
+        h[n] = a * h[n] + d * Bt[n * bc_stride] * xv;
+        y += Ct[n * bc_stride] * h[n];
+    }
+    return y;
+}
+
+/*
+ * Prompt scan over the flattened rows r = b * channels + c, r in
+ * [row_begin, row_end). Layouts (all contiguous, C order):
+ *   x, dt, z, y : [batch, channels, L]
+ *   Bm, Cm      : [batch, N, L]
+ *   A           : [channels, N];  D, dt_bias : [channels]
+ *   h0, h_last  : [batch, channels, N]
+ *   reset       : [batch, L] (uint8, nonzero = first token of a document)
+ *   states      : [batch, channels, L, N] (optional: state after every token)
+ * Optional pointers may be NULL: D (= 0), z (no gate), dt_bias (= 0),
+ * h0 (zeros), reset (none), h_last, states.
+ */
+int oracle_scan(int64_t batch, int64_t channels, int64_t N, int64_t L,
+                const double* x, const double* dt, const double* A,
+                const double* Bm, const double* Cm, const double* D, const double* z,
+                const double* dt_bias, const double* h0, const uint8_t* reset,
+                int dt_softplus, double* y, double* h_last, double* states,
+                int64_t row_begin, int64_t row_end) {
+    if (batch < 0 || channels < 0 || N < 1 || N > 4096 || L < 0) return ORACLE_BAD_ARG;
+    if (!x || !dt || !A || !Bm || !Cm || !y) return ORACLE_BAD_ARG;
+    if (row_begin < 0 || row_end > batch * channels || row_begin > row_end) return ORACLE_BAD_ARG;
+    double h[4096];
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const int64_t b = r / channels, c = r % channels;
+        for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[r * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t i = r * L + t;
+            const double d = step_size(dt[i], dt_bias, c, dt_softplus);
+            const int rs = reset ? (reset[b * L + t] != 0) : 0;
+            double yt = s6_token(N, h, d, x[i], A + c * N, Bm + b * N * L + t, Cm + b * N * L + t, L, rs);
+            yt += (D ? D[c] : 0.0) * x[i];
+            if (z) yt *= silu(z[i]);
+            y[i] = yt;
+            if (states)
+                for (int64_t n = 0; n < N; ++n) states[i * N + n] = h[n];
+        }
+        if (h_last)
+            for (int64_t n = 0; n < N; ++n) h_last[r * N + n] = h[n];
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Single-token decode step (nnterp "selective_scan" page: the state-update
+ * kernel call on one token; the updated state is what the cache receives).
+ *   state       : [batch, channels, N], read and written in place
+ *   x, dt, z, y : [batch, channels]
+ *   Bm, Cm      : [batch, N]
+ * Rows r = b * channels + c in [row_begin, row_end).
+ */
+int oracle_update(int64_t batch, int64_t channels, int64_t N,
+                  double* state, const double* x, const double* dt, const double* A,
+                  const double* Bm, const double* Cm, const double* D, const double* z,
+                  const double* dt_bias, int dt_softplus, double* y,
+                  int64_t row_begin, int64_t row_end) {
+    if (batch < 0 || channels < 0 || N < 1 || N > 4096) return ORACLE_BAD_ARG;
+    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return ORACLE_BAD_ARG;
+    if (row_begin < 0 || row_end > batch * channels || row_begin > row_end) return ORACLE_BAD_ARG;
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const int64_t b = r / channels, c = r % channels;
+        const double d = step_size(dt[r], dt_bias, c, dt_softplus);
+        double yt = s6_token(N, state + r * N, d, x[r], A + c * N, Bm + b * N, Cm + b * N, 1, 0);
+        yt += (D ? D[c] : 0.0) * x[r];
+        if (z) yt *= silu(z[r]);
+        y[r] = yt;
+    }
+    return ORACLE_OK;
+}

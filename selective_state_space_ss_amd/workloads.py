@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+scan's arithmetic, so both the HIP path and the CPU oracle can be fed from it.
+
+The five workloads are Mamba-1 S6 selective-scan calls at the shapes the method
+is used at (nnterp "selective_scan" page, class docstring: channel-first kernel
+tensors x, dt [batch, channels, seq], B, C [batch, state_dim, seq], A
+[channels, state_dim], a decode step drops the seq axis; mixle
+"selective_scan" page, module doc: S4D-real initialisation of A).
+
+Recipe (all draws fp32 from one ``torch.Generator`` seeded per workload, in
+the fixed order x, dt_raw, z, B, C, D, dt_bias, h0/state, reset; draws a
+workload does not use are skipped; ``N(mu, s)`` means ``mu + s * randn``;
+bf16 tensors are the fp32 draws rounded to nearest-even by ``Tensor.to``):
+
+* ``A[c, n] = -(n + 1)`` (S4D-real).
+* ``x, B, C, z, D ~ N(0, 1)``; ``dt_raw ~ N(0, 1)``.
+* ``dt_bias ~ N(-4, 0.5)`` per channel, except ``mamba130m`` where
+  ``dt_bias = softplus^-1(u)``, ``u = exp(Uniform(ln 1e-3, ln 0.1))``.
+* ``mamba2p8b``: ``h0 ~ N(0, 0.1)``; ``decode``: cached ``state ~ N(0, 1)``.
+* ``packed_reset``: ``reset[b, 0] = 1`` and ``reset[b, t >= 1]`` i.i.d.
+  Bernoulli(1/512), i.e. geometric document lengths with mean 512 (the last
+  document of a row is cut by the row's end).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    channels: int
+    state_dim: int
+    seqlen: int           # 0 marks the single-token decode step (no seq axis)
+    io_dtype: str         # "f32" or "bf16": dtype of x, dt, z, B, C and y
+    gate: bool            # silu(z) gate on
+    h0: Optional[float]   # std of the random initial / cached state, or None
+    reset_mean_doc: Optional[int]  # mean document length of the reset mask
+    dt_bias: str          # "normal" (N(-4, 0.5)) or "loguniform"
+    seed: int
+    note: str
+
+    @property
+    def decode(self) -> bool:
+        return self.seqlen == 0
+
+    @property
+    def channel_tokens(self) -> int:
+        return self.batch * self.channels * max(self.seqlen, 1)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32", 1, 8, 4, 64, "f32", False, None, None, "normal", 1001,
+                 "tiny S6 prompt scan, fp32, zero initial state, no gate"),
+        Workload("mamba130m", 4, 1536, 16, 2048, "bf16", True, None, None, "loguniform", 1002,
+                 "Mamba-130M-shaped layer (d_inner 1536), gated"),
+        Workload("mamba2p8b", 8, 5120, 16, 2048, "bf16", True, 0.1, None, "normal", 1003,
+                 "Mamba-2.8B-shaped layer (d_inner 5120), gated, random h0"),
+        Workload("packed_reset", 4, 2048, 16, 8192, "bf16", False, None, 512, "normal", 1004,
+                 "packed sequences with hard reset at document starts"),
+        Workload("decode", 256, 5120, 16, 0, "bf16", True, 1.0, None, "normal", 1005,
+                 "single-token decode step, cached fp32 state updated in place"),
+    ]
+}
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def io_torch_dtype(w: Workload) -> torch.dtype:
+    return _TORCH_DTYPE[w.io_dtype]
+
+
+def _normal(gen: torch.Generator, shape, mean: float = 0.0, std: float = 1.0) -> torch.Tensor:
+    t = torch.empty(shape, dtype=torch.float32)
+    t.normal_(generator=gen)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t
+
+
+def s4d_real_A(channels: int, state_dim: int) -> torch.Tensor:
+    """A[c, n] = -(n + 1), the S4D-real initialisation."""
+    row = -torch.arange(1, state_dim + 1, dtype=torch.float32)
+    return row.unsqueeze(0).expand(channels, state_dim).contiguous()
+
+
+def reset_mask(gen: torch.Generator, batch: int, seqlen: int, mean_doc: int) -> torch.Tensor:
+    """uint8 [batch, seqlen]; 1 marks the first token of a document."""
+    u = torch.rand((batch, seqlen), generator=gen)
+    m = (u < (1.0 / mean_doc)).to(torch.uint8)
+    if seqlen > 0:
+        m[:, 0] = 1
+    return m
+
+
+def make_inputs(w: Workload | str, seed: Optional[int] = None, *, batch: Optional[int] = None,
+                channels: Optional[int] = None, seqlen: Optional[int] = None,
+                state_dim: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one workload's inputs as CPU tensors.
+
+    Shape overrides keep the workload's distributions at another size (used
+    for small parity cases). Keys: x, dt, z, B, C, A, D, dt_bias, h0 (prompt)
+    or state (decode), reset; absent inputs are None.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    Bn = w.batch if batch is None else batch
+    Cn = w.channels if channels is None else channels
+    L = w.seqlen if seqlen is None else seqlen
+    N = w.state_dim if state_dim is None else state_dim
+    gen = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    io = io_torch_dtype(w)
+    tok = (Bn, Cn) if w.decode else (Bn, Cn, L)
+    bc = (Bn, N) if w.decode else (Bn, N, L)
+
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    out["x"] = _normal(gen, tok).to(io)
+    out["dt"] = _normal(gen, tok).to(io)
+    out["z"] = _normal(gen, tok).to(io) if w.gate else None
+    out["B"] = _normal(gen, bc).to(io)
+    out["C"] = _normal(gen, bc).to(io)
+    out["D"] = _normal(gen, (Cn,))
+    if w.dt_bias == "loguniform":
+        u = torch.empty((Cn,), dtype=torch.float32).uniform_(math.log(1e-3), math.log(0.1), generator=gen).exp()
+        # inverse of softplus: log(exp(u) - 1), evaluated in float64 for the small u
+        out["dt_bias"] = torch.log(torch.expm1(u.double())).float()
+    else:
+        out["dt_bias"] = _normal(gen, (Cn,), -4.0, 0.5)
+    h_shape = (Bn, Cn, N)
+    if w.decode:
+        out["state"] = _normal(gen, h_shape, 0.0, w.h0 if w.h0 is not None else 1.0)
+        out["h0"] = None
+    else:
+        out["h0"] = _normal(gen, h_shape, 0.0, w.h0) if w.h0 is not None else None
+    out["reset"] = (reset_mask(gen, Bn, L, w.reset_mean_doc)
+                    if (w.reset_mean_doc is not None and not w.decode) else None)
+    out["A"] = s4d_real_A(Cn, N)
+    return out
+
+
+def algorithmic_bytes(w: Workload) -> int:
+    """Bytes the method must move once: every input read once, every output
+    written once (the per-token state is never materialised)."""
+    s = 2 if w.io_dtype == "bf16" else 4
+    Bn, Cn, N = w.batch, w.channels, w.state_dim
+    L = max(w.seqlen, 1)
+    tok = Bn * Cn * L
+    n = 0
+    n += tok * s * (2 + (1 if w.gate else 0))   # x, dt (, z)
+    n += tok * s                                # y
+    n += 2 * Bn * N * L * s                     # B, C
+    n += Cn * N * 4 + 2 * Cn * 4                # A, D, dt_bias
+    if w.decode:
+        n += 2 * Bn * Cn * N * 4                # state read + write
+    else:
+        if w.h0 is not None:
+            n += Bn * Cn * N * 4                # h0
+        n += Bn * Cn * N * 4                    # h_last
+        if w.reset_mean_doc is not None:
+            n += Bn * L                         # reset mask
+    return n

@@ -1,0 +1,82 @@
+"""The oracle's pins must catch plausible mistakes: each mutant below plants
+one mistake in a copy of the oracle's C source (built into a temporary
+library on the CPU), and at least one pin in test_oracle_pins.py has to fail
+against it."""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
+
+MUTANTS = {
+    "decay_sign": ("exp(d * A_row[n])", "exp(-d * A_row[n])"),
+    "b_not_discretised": ("d * Bt[n * bc_stride] * xv", "Bt[n * bc_stride] * xv"),
+    "B_C_swapped": ("s6_token(N, h, d, x[i], A + c * N, Bm + b * N * L + t, Cm + b * N * L + t, L, rs)",
+                    "s6_token(N, h, d, x[i], A + c * N, Cm + b * N * L + t, Bm + b * N * L + t, L, rs)"),
+    "y_reads_old_state": ("h[n] = a * h[n] + d * Bt[n * bc_stride] * xv;\n        y += Ct[n * bc_stride] * h[n];",
+                          "y += Ct[n * bc_stride] * h[n];\n        h[n] = a * h[n] + d * Bt[n * bc_stride] * xv;"),
+    "skip_term_dropped": ("yt += (D ? D[c] : 0.0) * x[i];", "yt += 0.0;"),
+    "gate_before_skip": ("yt += (D ? D[c] : 0.0) * x[i];\n            if (z) yt *= silu(z[i]);",
+                         "if (z) yt *= silu(z[i]);\n            yt += (D ? D[c] : 0.0) * x[i];"),
+    "softplus_wrong": ("return fmax(v, 0.0) + log1p(exp(-fabs(v)));", "return fmax(v, 0.0) + exp(-fabs(v));"),
+    "bias_ignored": ("double v = dt_raw + (dt_bias ? dt_bias[c] : 0.0);", "double v = dt_raw;"),
+    "reset_zeroes_write_too": ("h[n] = a * h[n] + d * Bt[n * bc_stride] * xv;",
+                               "h[n] = reset ? 0.0 : a * h[n] + d * Bt[n * bc_stride] * xv;"),
+    "reset_ignored": ("double a = reset ? 0.0 : exp(d * A_row[n]);", "double a = exp(d * A_row[n]);"),
+    "A_wrong_index": ("exp(d * A_row[n])", "exp(d * A_row[0])"),
+    "h0_ignored": ("h[n] = h0 ? h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
+    "silu_is_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "decode_no_skip": ("yt += (D ? D[c] : 0.0) * x[r];", "yt += 0.0;"),
+}
+
+
+def _pin_callables():
+    calls = []
+    for name in dir(pins):
+        if not name.startswith("test_pin"):
+            continue
+        fn = getattr(pins, name)
+        if name == "test_pin6_hand_worked_cases":
+            for case in pins._hand_cases():
+                calls.append((f"{name}[{case['name']}]", lambda fn=fn, case=case: fn(case)))
+        else:
+            calls.append((name, fn))
+    return calls
+
+
+def _build_mutant(old, new, tmp):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site not unique: {old!r}"
+    path_c = os.path.join(tmp, "mut.c")
+    path_so = os.path.join(tmp, "mut.so")
+    with open(path_c, "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", path_so, path_c, "-lm"])
+    return path_so
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_mutant(mutant, monkeypatch):
+    old, new = MUTANTS[mutant]
+    real = oracle._load()
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(old, new, tmp)
+        lib = ctypes.CDLL(so)
+        for fn in ("oracle_scan", "oracle_update", "oracle_softplus"):
+            getattr(lib, fn).restype = getattr(real, fn).restype
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        monkeypatch.setattr(oracle, "_lib", lib)
+        failed = []
+        for name, call in _pin_callables():
+            try:
+                call()
+            except AssertionError:
+                failed.append(name)
+        assert failed, f"no pin catches mutant {mutant}"
