@@ -1,0 +1,119 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) Mamba-1 S6 selective scan.
+ *
+ * The method (nnterp "selective_scan" page, class docstring; TransformerLens
+ * "ssm_mixer" page, compute_ssm_state): per batch row b and channel c, with a
+ * state h of state_dim numbers,
+ *
+ *   dt_t = softplus(dt_t + dt_bias[c])        (dt_softplus != 0)
+ *        = dt_t + dt_bias[c]                  (dt_softplus == 0)
+ *   h_t  = exp(dt_t * A[c,:]) * h_{t-1} + dt_t * B[b,:,t] * x_t
+ *   y_t  = (C[b,:,t] . h_t + D[c] * x_t) * silu(z_t)    (gate when z != NULL)
+ *
+ * computed in fp32 with the state held in fp32. The calls mirror the two
+ * kernel calls the nnterp page names: the prompt scan
+ * (x, dt, A, B, C, D=, z=, delta_bias=) and the single-token state update
+ * (state, x, dt, A, B, C, D, z=, dt_bias=), and take the kernel's
+ * channel-first layouts from the same page.
+ *
+ * Conventions shared by both calls:
+ *  - All tensor pointers are DEVICE pointers to contiguous C-order arrays;
+ *    the caller owns every buffer. The library allocates nothing and keeps no
+ *    state between calls; calls are thread-safe.
+ *  - io_dtype (ss_dtype) is the element type of x, dt, z, B, C and y.
+ *    A, D, dt_bias, h0, h_last and state are always float32.
+ *  - The call enqueues its kernel on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns without synchronising.
+ *  - Arguments are validated before anything is enqueued; a validation
+ *    error returns its ss_status with no side effect. A failed launch returns
+ *    SS_ERR_HIP.
+ *  - Inputs are never modified (the decode state excepted). Outputs must not
+ *    overlap inputs, except h_last == h0 (same pointer) in the scan and the
+ *    in-place state of the decode step.
+ *  - state_dim must be in [1, 16]; anything else is SS_ERR_UNSUPPORTED.
+ *  - Non-finite inputs are outside the contract.
+ *  - Results are bitwise identical run to run for the same inputs.
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_ABI_VERSION 1
+#define SS_MAX_STATE_DIM 16
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_NULL = 1,        /* a required pointer is NULL */
+  SS_ERR_SHAPE = 2,       /* a size is negative or an index would overflow */
+  SS_ERR_DTYPE = 3,       /* io_dtype is not an ss_dtype */
+  SS_ERR_UNSUPPORTED = 4, /* state_dim outside [1, SS_MAX_STATE_DIM] */
+  SS_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap */
+  SS_ERR_HIP = 6,         /* the HIP runtime failed to launch the kernel */
+  SS_ERR_ALIGN = 7        /* a pointer is not aligned to its element size */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/*
+ * Prompt / prefill scan over seqlen tokens.
+ *
+ *   x, dt, z, y : [batch, channels, seqlen]   io_dtype
+ *   B, C        : [batch, state_dim, seqlen]  io_dtype (one group: shared by
+ *                                             every channel of a batch row)
+ *   A           : [channels, state_dim]       float32 (negative rates)
+ *   D, dt_bias  : [channels]                  float32, NULL reads as zeros
+ *   z           : NULL = no gate
+ *   h0          : [batch, channels, state_dim] float32, NULL = zero state
+ *                 (a prompt's scan starts from zeros; nnterp page, attributes)
+ *   reset       : [batch, seqlen] uint8 or NULL. reset[b,t] != 0 marks the
+ *                 first token of a packed document: the state is zeroed
+ *                 before that token, i.e. its decay exp(dt_t*A) is replaced
+ *                 by 0 ("s6_reset" post, Enforced Boundary Resetting).
+ *   y           : output [batch, channels, seqlen] io_dtype
+ *   h_last      : output [batch, channels, state_dim] float32, the state
+ *                 after the last token (what the next call or decode step
+ *                 starts from; nnterp page, state_output), or NULL. It may
+ *                 be the same pointer as h0. With seqlen == 0 it receives
+ *                 the initial state.
+ *
+ * batch == 0 or channels == 0 is a no-op returning SS_OK.
+ */
+int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
+                const void* x, const void* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const float* h0,
+                const uint8_t* reset, int dt_softplus, void* y, float* h_last, void* stream);
+
+/*
+ * Single-token decode update of a cached state, in place (nnterp
+ * "selective_scan" page: the state-update call on one token; the updated
+ * state is what the cache receives and y reads it).
+ *
+ *   state       : [batch, channels, state_dim] float32, read and written
+ *   x, dt, z, y : [batch, channels]           io_dtype (z NULL = no gate)
+ *   B, C        : [batch, state_dim]          io_dtype
+ *   A           : [channels, state_dim]       float32
+ *   D, dt_bias  : [channels]                  float32, NULL reads as zeros
+ *
+ * batch == 0 or channels == 0 is a no-op returning SS_OK.
+ */
+int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_dtype, float* state,
+                    const void* x, const void* dt, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y,
+                    void* stream);
+
+/* Static, NUL-terminated name of a status code (unknown codes included). */
+const char* ss_status_str(int status);
+
+/* SS_ABI_VERSION of the built library. */
+int ss_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

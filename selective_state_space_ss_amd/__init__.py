@@ -1,0 +1,28 @@
+"""MI355X (gfx950) Mamba-1 S6 selective scan.
+
+The compute lives in the HIP library ``libssscan.so`` (C ABI declared in
+``include/ss_scan.h``); this package is its thin Python binding. The two
+entry points keep the C names and the argument order of the kernel calls on
+the nnterp "selective_scan" page:
+
+    ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
+                reset=None, dt_softplus=True) -> (y, h_last)
+    ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                    dt_softplus=True) -> y          (state updated in place)
+
+Arguments are torch tensors on the GPU: the binding checks them, allocates
+the outputs with torch and passes raw device pointers plus the current HIP
+stream. Every step of the computation runs in the library's kernels; there is
+no other implementation to fall back to, and a missing library is an error.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    SSError,
+    abi_version,
+    library_path,
+    load_library,
+    ss_scan_fwd,
+    ss_state_update,
+    status_str,
+)

@@ -1,0 +1,187 @@
+"""ctypes binding of libssscan.so: argument checks and marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssscan.so")
+
+SS_OK = 0
+SS_F32 = 0
+SS_BF16 = 1
+MAX_STATE_DIM = 16
+
+_lib = None
+
+
+class SSError(RuntimeError):
+    """A non-zero ss_status returned by the library."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_str(code)} (status {code})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssscan.so (built by ``python -m selective_state_space_ss_amd.build``).
+    There is no fallback: a missing library raises."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m selective_state_space_ss_amd.build` "
+            "(the selective scan has no implementation other than the HIP library)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.ss_scan_fwd.restype = i32
+    lib.ss_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp]
+    lib.ss_state_update.restype = i32
+    lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
+    lib.ss_status_str.restype = ctypes.c_char_p
+    lib.ss_status_str.argtypes = [i32]
+    lib.ss_abi_version.restype = i32
+    lib.ss_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load_library().ss_status_str(int(code)).decode()
+
+
+def abi_version() -> int:
+    return load_library().ss_abi_version()
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return SS_F32
+    if dtype == torch.bfloat16:
+        return SS_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {dtype}")
+
+
+def _check(t, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device, stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=None, dt_softplus: bool = True,
+                *, y=None, h_last=None, return_last_state: bool = True, stream=None) -> Tuple:
+    """Prompt scan on the GPU.
+
+    x, dt, z: [batch, channels, seq]; B, C: [batch, state_dim, seq] (float32 or
+    bfloat16, one dtype for all); A: [channels, state_dim]; D, dt_bias:
+    [channels]; h0: [batch, channels, state_dim]; reset: [batch, seq] uint8 or
+    bool (nonzero = first token of a document). A, D, dt_bias and h0 are
+    float32. Returns (y, h_last); h_last is None when return_last_state is
+    False. Preallocated outputs may be passed as y= and h_last= (h_last may be
+    h0 itself). Runs on the current torch stream unless stream= is given.
+    """
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, channels, seq]")
+    batch, channels, L = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ss_scan_fwd runs on the GPU: x must be a device tensor")
+    io = x.dtype
+    code = _io_code(io)
+    if A.dim() != 2 or A.shape[0] != channels:
+        raise ValueError("A must be [channels, state_dim]")
+    N = A.shape[1]
+    _check(x, "x", (batch, channels, L), io, dev)
+    _check(dt, "dt", (batch, channels, L), io, dev)
+    _check(A, "A", (channels, N), torch.float32, dev)
+    _check(B, "B", (batch, N, L), io, dev)
+    _check(C, "C", (batch, N, L), io, dev)
+    if D is not None:
+        _check(D, "D", (channels,), torch.float32, dev)
+    if z is not None:
+        _check(z, "z", (batch, channels, L), io, dev)
+    if dt_bias is not None:
+        _check(dt_bias, "dt_bias", (channels,), torch.float32, dev)
+    if h0 is not None:
+        _check(h0, "h0", (batch, channels, N), torch.float32, dev)
+    if reset is not None:
+        if reset.dtype == torch.bool:
+            reset = reset.view(torch.uint8)
+        _check(reset, "reset", (batch, L), torch.uint8, dev)
+    if y is None:
+        y = torch.empty((batch, channels, L), dtype=io, device=dev)
+    else:
+        _check(y, "y", (batch, channels, L), io, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((batch, channels, N), dtype=torch.float32, device=dev)
+    elif h_last is not None:
+        _check(h_last, "h_last", (batch, channels, N), torch.float32, dev)
+    lib = load_library()
+    rc = lib.ss_scan_fwd(batch, channels, N, L, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                         _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(reset), int(bool(dt_softplus)), _ptr(y),
+                         _ptr(h_last), _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_scan_fwd")
+    return y, h_last
+
+
+def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True, *, y=None,
+                    stream=None):
+    """Single-token decode step on the GPU; `state` ([batch, channels,
+    state_dim] float32) is updated in place. x, dt, z: [batch, channels];
+    B, C: [batch, state_dim]. Returns y [batch, channels]."""
+    import torch
+    if state.dim() != 3:
+        raise ValueError("state must be [batch, channels, state_dim]")
+    batch, channels, N = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("ss_state_update runs on the GPU: state must be a device tensor")
+    io = x.dtype
+    code = _io_code(io)
+    _check(state, "state", (batch, channels, N), torch.float32, dev)
+    _check(x, "x", (batch, channels), io, dev)
+    _check(dt, "dt", (batch, channels), io, dev)
+    _check(A, "A", (channels, N), torch.float32, dev)
+    _check(B, "B", (batch, N), io, dev)
+    _check(C, "C", (batch, N), io, dev)
+    if D is not None:
+        _check(D, "D", (channels,), torch.float32, dev)
+    if z is not None:
+        _check(z, "z", (batch, channels), io, dev)
+    if dt_bias is not None:
+        _check(dt_bias, "dt_bias", (channels,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((batch, channels), dtype=io, device=dev)
+    else:
+        _check(y, "y", (batch, channels), io, dev)
+    lib = load_library()
+    rc = lib.ss_state_update(batch, channels, N, code, _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
+                             _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_state_update")
+    return y

@@ -1,0 +1,99 @@
+// C ABI entry points: validate, pick the kernel instantiation, enqueue.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ss_scan.h"
+#include "ss_launch.h"
+#include "ss_validate.h"
+
+namespace {
+
+bool vec16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype, const void* x,
+                const void* dt, const float* A, const void* B, const void* C, const float* D, const void* z,
+                const float* dt_bias, const float* h0, const uint8_t* reset, int dt_softplus, void* y,
+                float* h_last, void* stream) {
+  const ss::ScanArgs a{batch, channels, state_dim, seqlen, io_dtype, x,     dt,          A,
+                       B,     C,        D,         z,      dt_bias,  h0,    reset, dt_softplus, y, h_last};
+  bool noop = false;
+  const ss_status st = ss::validate_scan(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (seqlen == 0 && h_last == nullptr) return SS_OK;
+  if (ss::scan_fwd_blocks(batch, channels) > 0x7fffffff) return SS_ERR_SHAPE;
+
+  const bool bf16 = io_dtype == SS_BF16;
+  const int64_t vec = bf16 ? 8 : 4;
+  ss::ScanParams p{};
+  p.batch = batch;
+  p.channels = channels;
+  p.L = seqlen;
+  p.N = (int)state_dim;
+  p.dt_softplus = dt_softplus != 0;
+  p.vec_ok = (seqlen % vec == 0) && vec16(x) && vec16(dt) && vec16(z) && vec16(y) && vec16(B) && vec16(C);
+  p.reset_vec = (seqlen % 16 == 0) && vec16(reset);
+  p.x = x;
+  p.dt = dt;
+  p.z = z;
+  p.B = B;
+  p.C = C;
+  p.A = A;
+  p.D = D;
+  p.dt_bias = dt_bias;
+  p.h0 = h0;
+  p.reset = reset;
+  p.y = y;
+  p.h_last = h_last;
+  const hipError_t e = ss::launch_scan_fwd(p, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_dtype, float* state, const void* x,
+                    const void* dt, const float* A, const void* B, const void* C, const float* D, const void* z,
+                    const float* dt_bias, int dt_softplus, void* y, void* stream) {
+  const ss::UpdateArgs a{batch, channels, state_dim, io_dtype, state, x,       dt,          A,
+                         B,     C,        D,         z,        dt_bias, dt_softplus, y};
+  bool noop = false;
+  const ss_status st = ss::validate_update(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (!ss::state_update_grid_ok(batch, channels)) return SS_ERR_SHAPE;
+  ss::UpdateParams p{};
+  p.batch = batch;
+  p.channels = channels;
+  p.N = (int)state_dim;
+  p.dt_softplus = dt_softplus != 0;
+  p.vec_ok = state_dim == 16 && vec16(state);
+  p.state = state;
+  p.x = x;
+  p.dt = dt;
+  p.z = z;
+  p.B = B;
+  p.C = C;
+  p.A = A;
+  p.D = D;
+  p.dt_bias = dt_bias;
+  p.y = y;
+  const hipError_t e = ss::launch_state_update(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+const char* ss_status_str(int status) {
+  switch (status) {
+    case SS_OK: return "SS_OK";
+    case SS_ERR_NULL: return "SS_ERR_NULL: a required pointer is NULL";
+    case SS_ERR_SHAPE: return "SS_ERR_SHAPE: a size is negative or too large";
+    case SS_ERR_DTYPE: return "SS_ERR_DTYPE: io_dtype is not SS_F32 or SS_BF16";
+    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 16]";
+    case SS_ERR_ALIAS: return "SS_ERR_ALIAS: an output overlaps an input";
+    case SS_ERR_HIP: return "SS_ERR_HIP: the HIP runtime failed to launch the kernel";
+    case SS_ERR_ALIGN: return "SS_ERR_ALIGN: a pointer is not aligned to its element size";
+    default: return "unknown ss_status";
+  }
+}
+
+int ss_abi_version(void) { return SS_ABI_VERSION; }
+
+}  // extern "C"

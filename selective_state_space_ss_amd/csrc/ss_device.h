@@ -1,0 +1,133 @@
+// Device-side helpers of the gfx950 selective-scan kernels: fp32 numerics,
+// bf16 load/store, and the 16-lane DPP scan of the associative pair (a, b).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- I/O types
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Io;
+
+template <>
+struct Io<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+
+template <>
+struct Io<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float to_f32(bf16_t v) { return __builtin_bit_cast(float, uint32_t(v.bits) << 16); }
+  __device__ static bf16_t from_f32(float v) {
+    __bf16 h = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32)
+    return bf16_t{__builtin_bit_cast(uint16_t, h)};
+  }
+};
+
+// Load kVec consecutive elements (16 bytes) and widen to fp32.
+__device__ __forceinline__ void load_vec16(const float* p, float* out) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+__device__ __forceinline__ void load_vec16(const bf16_t* p, float* out) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
+// Narrow and store kVec consecutive elements (16 bytes).
+__device__ __forceinline__ void store_vec16(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_vec16(bf16_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = Io<bf16_t>::from_f32(v[2 * i]).bits;
+    const uint32_t hi = Io<bf16_t>::from_f32(v[2 * i + 1]).bits;
+    w[i] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(u), u = e^{-|v|} in (0, 1].
+// log1p(u) is log(w) for w = fl(1 + u) plus the rounding error of that sum,
+// delta = u - (w - 1) (exact by Sterbenz), since log(1 + u) = log(w) +
+// log(1 + delta / w) and |delta| <= 2^-24 makes the second term delta to
+// within 2^-24 relative (the compensated log1p of Goldberg, 1991).
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float u = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+  const float w = 1.0f + u;
+  const float delta = u - (w - 1.0f);
+  const float l = __builtin_fmaf(fast_log2(w), kLn2, delta);
+  return __builtin_fmaxf(v, 0.0f) + l;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z}); e^{-z} = inf gives -0.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// ---------------------------------------------------------------- DPP
+// DPP control words (gfx9 encoding).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowNewBcast15 = 0x15F;  // lane 15 of each row to its whole row
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm:[1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm:[2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_or(float old, float v) {
+  // Lanes whose source is outside the row keep `old`.
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                               false));
+}
+
+// Inclusive scan over each 16-lane row of the affine pair (A, B), lane i
+// combining the elements of lanes 0..i of its row in order:
+//   (A1, B1) then (A2, B2)  ->  (A2 * A1, A2 * B1 + B2)
+// (the composition h -> A2 (A1 h + B1) + B2; "s6_reset" post, Associative
+// Boundary Resetting, binop). Hillis-Steele steps of 1, 2, 4, 8 lanes; a lane
+// whose partner falls outside the row has its DPP write disabled and keeps its
+// value, which is combining with the identity (1, 0). In each step the B
+// update reads the lane's A before the A update overwrites it. The leading
+// s_nop covers the VALU-write -> DPP-read wait states (2 on gfx9); inside
+// the block each DPP read is at least 3 instructions after the write.
+__device__ __forceinline__ void row16_inclusive_scan(float& A, float& B) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B));
+}
+
+}  // namespace ss

@@ -1,0 +1,58 @@
+// Kernel parameter blocks and launchers shared by the C ABI (ss_abi.hip) and
+// the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+struct ScanParams {
+  int64_t batch, channels, L;
+  int64_t chan_blocks;  // ceil(channels / channels per block)
+  int N;
+  int dt_softplus;
+  int vec_ok;    // x, dt, z, y, B, C are 16-byte aligned and L is a multiple of the vector width
+  int reset_vec; // reset is 16-byte aligned and L is a multiple of 16
+  const void* x;
+  const void* dt;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* h0;
+  const uint8_t* reset;
+  void* y;
+  float* h_last;
+};
+
+struct UpdateParams {
+  int64_t batch, channels;
+  int N;
+  int dt_softplus;
+  int vec_ok;  // state 16-byte aligned and N == 16
+  float* state;
+  const void* x;
+  const void* dt;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  void* y;
+};
+
+// io_bf16: element type of x, dt, z, B, C, y (false = float32).
+hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream);
+hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
+
+}  // namespace ss
+
+namespace ss {
+// Launch-geometry limits, checked by the C ABI before launching.
+int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
+bool state_update_grid_ok(int64_t batch, int64_t channels);
+}  // namespace ss

@@ -1,0 +1,140 @@
+// Host-only argument checks of the C ABI. No HIP dependency: the same code is
+// compiled into the library and into a plain g++ test.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/ss_scan.h"
+
+namespace ss {
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  Span() = default;
+  Span(const void* p, int64_t bytes) {
+    if (p && bytes > 0) {
+      lo = reinterpret_cast<uintptr_t>(p);
+      hi = lo + static_cast<uintptr_t>(bytes);
+    }
+  }
+  bool empty() const { return lo == hi; }
+  bool overlaps(const Span& o) const { return !empty() && !o.empty() && lo < o.hi && o.lo < hi; }
+};
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+inline bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// Inputs of the prompt scan, in ABI order; see ss_scan_fwd in ss_scan.h.
+struct ScanArgs {
+  int64_t batch, channels, state_dim, seqlen;
+  int io_dtype;
+  const void *x, *dt;
+  const float* A;
+  const void *B, *C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  const float* h0;
+  const uint8_t* reset;
+  int dt_softplus;
+  void* y;
+  float* h_last;
+};
+
+// SS_OK means "launch"; *noop set means "valid and nothing to do".
+inline ss_status validate_scan(const ScanArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.channels < 0 || a.seqlen < 0 || a.state_dim < 0) return SS_ERR_SHAPE;
+  if (a.state_dim < 1 || a.state_dim > SS_MAX_STATE_DIM) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0 || a.channels == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t rows, tok, tok_bytes, bcn, bc_bytes, st, st_bytes, cn, a_bytes, rs_bytes;
+  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, a.seqlen, &tok) || !mul_ok(tok, es, &tok_bytes) ||
+      !mul_ok(a.batch, a.state_dim, &bcn) || !mul_ok(bcn, a.seqlen, &bcn) || !mul_ok(bcn, es, &bc_bytes) ||
+      !mul_ok(rows, a.state_dim, &st) || !mul_ok(st, 4, &st_bytes) || !mul_ok(a.channels, a.state_dim, &cn) ||
+      !mul_ok(cn, 4, &a_bytes) || !mul_ok(a.batch, a.seqlen, &rs_bytes))
+    return SS_ERR_SHAPE;
+  if (tok_bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  const bool has_tokens = a.seqlen > 0;
+  if (!a.A) return SS_ERR_NULL;
+  if (has_tokens && (!a.x || !a.dt || !a.B || !a.C || !a.y)) return SS_ERR_NULL;
+  const void* io_ptrs[] = {a.x, a.dt, a.z, a.B, a.C, a.y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+  const void* f32_ptrs[] = {a.A, a.D, a.dt_bias, a.h0, a.h_last};
+  for (const void* p : f32_ptrs)
+    if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+
+  const Span x(a.x, has_tokens ? tok_bytes : 0), dt(a.dt, has_tokens ? tok_bytes : 0),
+      z(a.z, has_tokens ? tok_bytes : 0), B(a.B, has_tokens ? bc_bytes : 0), C(a.C, has_tokens ? bc_bytes : 0),
+      A(a.A, a_bytes), D(a.D, a.channels * 4), bias(a.dt_bias, a.channels * 4), h0(a.h0, st_bytes),
+      reset(a.reset, has_tokens ? rs_bytes : 0), y(a.y, has_tokens ? tok_bytes : 0), hl(a.h_last, st_bytes);
+  const Span inputs[] = {x, dt, z, B, C, A, D, bias, h0, reset};
+  for (const Span& in : inputs) {
+    if (y.overlaps(in)) return SS_ERR_ALIAS;
+    if (&in != &inputs[8] && hl.overlaps(in)) return SS_ERR_ALIAS;
+  }
+  if (hl.overlaps(h0) && a.h_last != a.h0) return SS_ERR_ALIAS;
+  if (y.overlaps(hl)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
+// Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
+struct UpdateArgs {
+  int64_t batch, channels, state_dim;
+  int io_dtype;
+  float* state;
+  const void *x, *dt;
+  const float* A;
+  const void *B, *C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  int dt_softplus;
+  void* y;
+};
+
+inline ss_status validate_update(const UpdateArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.channels < 0 || a.state_dim < 0) return SS_ERR_SHAPE;
+  if (a.state_dim < 1 || a.state_dim > SS_MAX_STATE_DIM) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0 || a.channels == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t rows, tok_bytes, st, st_bytes, bcn, bc_bytes, cn, a_bytes;
+  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, es, &tok_bytes) || !mul_ok(rows, a.state_dim, &st) ||
+      !mul_ok(st, 4, &st_bytes) || !mul_ok(a.batch, a.state_dim, &bcn) || !mul_ok(bcn, es, &bc_bytes) ||
+      !mul_ok(a.channels, a.state_dim, &cn) || !mul_ok(cn, 4, &a_bytes))
+    return SS_ERR_SHAPE;
+  if (st_bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  if (!a.state || !a.x || !a.dt || !a.A || !a.B || !a.C || !a.y) return SS_ERR_NULL;
+  const void* io_ptrs[] = {a.x, a.dt, a.z, a.B, a.C, a.y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+  const void* f32_ptrs[] = {a.state, a.A, a.D, a.dt_bias};
+  for (const void* p : f32_ptrs)
+    if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+  const Span state(a.state, st_bytes), x(a.x, tok_bytes), dt(a.dt, tok_bytes), z(a.z, tok_bytes),
+      B(a.B, bc_bytes), C(a.C, bc_bytes), A(a.A, a_bytes), D(a.D, a.channels * 4), bias(a.dt_bias, a.channels * 4),
+      y(a.y, tok_bytes);
+  const Span inputs[] = {x, dt, z, B, C, A, D, bias};
+  for (const Span& in : inputs)
+    if (y.overlaps(in) || state.overlaps(in)) return SS_ERR_ALIAS;
+  if (y.overlaps(state)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
+}  // namespace ss

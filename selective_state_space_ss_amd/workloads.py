@@ -170,3 +170,24 @@ def algorithmic_bytes(w: Workload) -> int:
         if w.reset_mean_doc is not None:
             n += Bn * L                         # reset mask
     return n
+
+
+def make_case(seed: int, batch: int, channels: int, state_dim: int, seqlen: int, io_dtype: str = "bf16",
+              gate: bool = True, h0: bool = True, reset_mean_doc: Optional[int] = None,
+              dt_bias: str = "normal") -> Dict[str, Optional[torch.Tensor]]:
+    """An arbitrary-shape prompt case with the workloads' distributions
+    (h0 ~ N(0, 0.1) when requested); seqlen == 0 is allowed. Same key set as
+    make_inputs."""
+    w = Workload("case", batch, channels, state_dim, max(seqlen, 1), io_dtype, gate, 0.1 if h0 else None,
+                 reset_mean_doc, dt_bias, seed, "parity case")
+    out = make_inputs(w, seqlen=seqlen)
+    return out
+
+
+def make_decode_case(seed: int, batch: int, channels: int, state_dim: int, io_dtype: str = "bf16",
+                     gate: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """An arbitrary-shape decode-step case with the decode workload's
+    distributions."""
+    w = Workload("decode_case", batch, channels, state_dim, 0, io_dtype, gate, 1.0, None, "normal", seed,
+                 "decode parity case")
+    return make_inputs(w)

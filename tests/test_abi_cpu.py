@@ -1,0 +1,112 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import selective_state_space_ss_amd as ss
+from selective_state_space_ss_amd._binding import load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_scan.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, HIP, ALIGN = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ss_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ss.library_path()):
+        from selective_state_space_ss_amd.build import build
+        build()
+    return load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["ss_abi_version", "ss_scan_fwd", "ss_state_update", "ss_status_str"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", ss.library_path()], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_status_strings_and_version(lib):
+    assert ss.abi_version() == 1
+    for code in range(8):
+        assert ss.status_str(code).startswith("SS_")
+    assert "unknown" in ss.status_str(99)
+
+
+# Fake, well-aligned, disjoint "device" addresses: validation never dereferences them.
+MB = 1 << 20
+
+
+def scan_call(lib, batch=2, channels=8, N=16, L=64, io=1, x=1 * MB, dt=2 * MB, A=3 * MB, B=4 * MB, C=5 * MB,
+              D=None, z=None, bias=None, h0=None, reset=None, y=6 * MB, h_last=None):
+    return lib.ss_scan_fwd(batch, channels, N, L, io, x, dt, A, B, C, D, z, bias, h0, reset, 1, y, h_last, None)
+
+
+def upd_call(lib, batch=2, channels=8, N=16, io=1, state=1 * MB, x=2 * MB, dt=3 * MB, A=4 * MB, B=5 * MB, C=6 * MB,
+             D=None, z=None, bias=None, y=7 * MB):
+    return lib.ss_state_update(batch, channels, N, io, state, x, dt, A, B, C, D, z, bias, 1, y, None)
+
+
+def test_scan_validation(lib):
+    assert scan_call(lib, io=2) == DTYPE
+    assert scan_call(lib, batch=-1) == SHAPE
+    assert scan_call(lib, L=-5) == SHAPE
+    assert scan_call(lib, N=0) == UNSUP
+    assert scan_call(lib, N=17) == UNSUP
+    assert scan_call(lib, x=None) == NULL
+    assert scan_call(lib, y=None) == NULL
+    assert scan_call(lib, A=None) == NULL
+    assert scan_call(lib, x=1 * MB + 1) == ALIGN          # bf16 needs 2-byte alignment
+    assert scan_call(lib, io=0, y=6 * MB + 2) == ALIGN    # fp32 needs 4-byte alignment
+    assert scan_call(lib, y=1 * MB) == ALIAS               # y over x
+    assert scan_call(lib, y=1 * MB + 128) == ALIAS         # partial overlap
+    assert scan_call(lib, h0=7 * MB, h_last=7 * MB + 64) == ALIAS
+    assert scan_call(lib, h_last=4 * MB) == ALIAS          # h_last over B
+    assert scan_call(lib, batch=1 << 40, channels=1 << 40) == SHAPE
+    # empty problems are valid no-ops and never reach the device
+    assert scan_call(lib, batch=0) == OK
+    assert scan_call(lib, channels=0, x=None, dt=None, B=None, C=None, y=None) == OK
+
+
+def test_update_validation(lib):
+    assert upd_call(lib, io=7) == DTYPE
+    assert upd_call(lib, N=17) == UNSUP
+    assert upd_call(lib, state=None) == NULL
+    assert upd_call(lib, y=2 * MB) == ALIAS
+    assert upd_call(lib, state=2 * MB) == ALIAS
+    assert upd_call(lib, state=1 * MB + 2) == ALIGN
+    assert upd_call(lib, batch=0) == OK
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    x = torch.zeros(1, 2, 3)
+    with pytest.raises(ValueError):
+        ss.ss_scan_fwd(x, x, torch.zeros(2, 4), torch.zeros(1, 4, 3), torch.zeros(1, 4, 3))
+
+
+def test_validator_header_builds_standalone(tmp_path):
+    """The validation header has no HIP dependency (host-only g++ build)."""
+    src = tmp_path / "t.cpp"
+    src.write_text('#include "ss_validate.h"\nint main(){ss::ScanArgs a{}; bool n; return ss::validate_scan(a,&n)==SS_ERR_UNSUPPORTED?0:1;}\n')
+    exe = tmp_path / "t"
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I",
+                    os.path.join(ROOT, "selective_state_space_ss_amd", "csrc"), str(src), "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on
+the five workloads and on ragged and degenerate shapes.
+
+Tolerances (tests/helpers.py): fp32 I/O |d| <= 1e-5 + 1e-4 |ref|; bf16 I/O
+|d| <= 1e-4 + 2e-2 |ref|; the fp32 final / cached state at the fp32 bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_ss_amd as ss
+from selective_state_space_ss_amd.workloads import WORKLOADS, make_case, make_decode_case, make_inputs
+from tests.helpers import (TOL, TOL_STATE, check_close, io_name, np64, oracle_scan_full, oracle_scan_rows,
+                           sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_scan(inp, dt_softplus=True, **kw):
+    d = to_dev(inp)
+    y, h = ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d.get("z"), dt_bias=d["dt_bias"],
+                          h0=d.get("h0"), reset=d.get("reset"), dt_softplus=dt_softplus, **kw)
+    torch.cuda.synchronize()
+    return y, h
+
+
+def compare_full(inp, dt_softplus=True, what=""):
+    y, h = run_scan(inp, dt_softplus)
+    yr, hr = oracle_scan_full(inp, dt_softplus)
+    rtol, atol = TOL[io_name(inp["x"])]
+    s = check_close(np64(y), yr, rtol, atol, f"y {what}")
+    check_close(np64(h), hr, *TOL_STATE, f"h_last {what}")
+    return s
+
+
+# ------------------------------------------------------------------ workloads
+def test_workload_tiny_fp32():
+    inp = make_inputs("tiny_fp32")
+    print("workload tiny_fp32", flush=True)
+    compare_full(inp, what="tiny_fp32")
+
+
+@pytest.mark.parametrize("name", ["mamba130m", "mamba2p8b", "packed_reset"])
+def test_workload_full_size_sampled_rows(name):
+    """The full-size launch (the benchmark's), checked on sampled rows."""
+    w = WORKLOADS[name]
+    print(f"workload {name} full size", flush=True)
+    inp = make_inputs(name)
+    y, h = run_scan(inp)
+    rows = sample_rows(w.batch, w.channels, 40, seed=7)
+    yr, hr = oracle_scan_rows(inp, rows)
+    yg = np.stack([np64(y[b, c]) for b, c in rows])
+    hg = np.stack([np64(h[b, c]) for b, c in rows])
+    rtol, atol = TOL[w.io_dtype]
+    check_close(yg, yr, rtol, atol, f"y {name}")
+    check_close(hg, hr, *TOL_STATE, f"h_last {name}")
+    assert torch.isfinite(y.float()).all() and torch.isfinite(h).all()
+
+
+def test_workload_decode_full():
+    w = WORKLOADS["decode"]
+    print("workload decode", flush=True)
+    inp = make_inputs("decode")
+    d = to_dev(inp)
+    state = d["state"].clone()
+    y = ss.ss_state_update(state, d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                           dt_bias=d["dt_bias"])
+    torch.cuda.synchronize()
+    yr, sr = oracle.state_update(np64(inp["state"]), np64(inp["x"]), np64(inp["dt"]), np64(inp["A"]),
+                                 np64(inp["B"]), np64(inp["C"]), D=np64(inp["D"]), z=np64(inp["z"]),
+                                 dt_bias=np64(inp["dt_bias"]))
+    check_close(np64(y), yr, *TOL[w.io_dtype], "decode y")
+    check_close(np64(state), sr, *TOL_STATE, "decode state")
+
+
+# ------------------------------------------------------------------ ragged / tiles
+RAGGED = [
+    # io, L, gate, h0, reset
+    ("f32", 1, False, False, None), ("f32", 7, True, True, None), ("f32", 255, True, False, None),
+    ("f32", 256, False, True, 16), ("f32", 257, True, True, 8), ("f32", 1000, True, True, None),
+    ("bf16", 1, True, True, None), ("bf16", 15, False, False, 4), ("bf16", 511, True, True, None),
+    ("bf16", 512, True, True, None), ("bf16", 513, True, False, None), ("bf16", 1024, False, True, 64),
+    ("bf16", 1543, True, True, None), ("bf16", 2048, True, True, None), ("bf16", 2049, False, False, 100),
+    ("bf16", 4100, True, True, 512),
+]
+
+
+@pytest.mark.parametrize("io,L,gate,h0,reset", RAGGED, ids=[f"{r[0]}-L{r[1]}-g{int(r[2])}-h{int(r[3])}-r{r[4]}"
+                                                            for r in RAGGED])
+def test_ragged_shapes(io, L, gate, h0, reset):
+    """Chunks of 256 or 512 tokens, a ragged tail, channels not a multiple of
+    the block's 16."""
+    print(f"ragged io={io} L={L} gate={gate} h0={h0} reset={reset}", flush=True)
+    inp = make_case(100 + L, 2, 19, 16, L, io, gate=gate, h0=h0, reset_mean_doc=reset)
+    compare_full(inp, what=f"{io} L={L}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_state_dims(io, N):
+    print(f"state_dim io={io} N={N}", flush=True)
+    inp = make_case(200 + N, 3, 5, N, 300, io, gate=True, h0=True, reset_mean_doc=50)
+    compare_full(inp, what=f"{io} N={N}")
+
+
+def test_softplus_off_and_optional_inputs_absent():
+    inp = make_case(301, 2, 17, 16, 600, "f32", gate=False, h0=False)
+    inp["D"] = None
+    inp["dt_bias"] = None
+    inp["dt"] = (inp["dt"].abs() * 0.05).contiguous()  # a positive step size without softplus
+    y, h = run_scan(inp, dt_softplus=False)
+    yr, hr = oracle.scan(np64(inp["x"]), np64(inp["dt"]), np64(inp["A"]), np64(inp["B"]), np64(inp["C"]),
+                         dt_softplus=False)
+    check_close(np64(y), yr, *TOL["f32"], "y softplus off")
+    check_close(np64(h), hr, *TOL_STATE, "h_last softplus off")
+
+
+def test_seqlen_zero_returns_initial_state():
+    inp = make_case(302, 2, 5, 16, 0, "bf16", gate=True, h0=True)
+    y, h = run_scan(inp)
+    assert y.numel() == 0
+    assert torch.equal(h.cpu(), inp["h0"])
+    inp["h0"] = None
+    _, h = run_scan(inp)
+    assert torch.count_nonzero(h) == 0
+
+
+def test_empty_batch_and_channels_are_noops():
+    for b, c in [(0, 5), (2, 0)]:
+        inp = make_case(303, b, c, 16, 32, "bf16")
+        y, h = run_scan(inp)
+        assert y.numel() == 0 and h.numel() == 0
+
+
+# ------------------------------------------------------------------ numerics
+def test_softplus_accuracy():
+    """L = 1, N = 1, B = C = x = 1, zero state: y = dt = softplus(dt_raw)."""
+    v = torch.linspace(-30, 30, 6001, dtype=torch.float32)
+    ch = v.numel()
+    inp = dict(x=torch.ones(1, ch, 1), dt=v.view(1, ch, 1).clone(), A=-torch.ones(ch, 1), B=torch.ones(1, 1, 1),
+               C=torch.ones(1, 1, 1), D=None, z=None, dt_bias=None, h0=None, reset=None)
+    y, _ = run_scan(inp)
+    ref = np.logaddexp(0.0, v.double().numpy())
+    check_close(np64(y)[0, :, 0], ref, 2e-6, 1e-30, "softplus")
+
+
+def test_gate_accuracy():
+    """B = 0, D = 1, x = 1: y = silu(z)."""
+    z = torch.linspace(-40, 40, 8001, dtype=torch.float32)
+    ch = z.numel()
+    inp = dict(x=torch.ones(1, ch, 1), dt=torch.zeros(1, ch, 1), A=-torch.ones(ch, 1), B=torch.zeros(1, 1, 1),
+               C=torch.ones(1, 1, 1), D=torch.ones(ch), z=z.view(1, ch, 1).clone(), dt_bias=None, h0=None,
+               reset=None)
+    y, _ = run_scan(inp)
+    zz = z.double().numpy()
+    ref = zz / (1.0 + np.exp(-zz))
+    check_close(np64(y)[0, :, 0], ref, 2e-6, 1e-30, "silu")
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N,gate", [(1, True), (3, False), (4, True), (9, True), (16, False), (16, True)])
+def test_decode_shapes(io, N, gate):
+    print(f"decode io={io} N={N} gate={gate}", flush=True)
+    inp = make_decode_case(400 + N, 7, 37, N, io, gate=gate)
+    d = to_dev(inp)
+    state = d["state"].clone()
+    y = ss.ss_state_update(state, d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d.get("z"),
+                           dt_bias=d["dt_bias"])
+    torch.cuda.synchronize()
+    yr, sr = oracle.state_update(np64(inp["state"]), np64(inp["x"]), np64(inp["dt"]), np64(inp["A"]),
+                                 np64(inp["B"]), np64(inp["C"]), D=np64(inp["D"]), z=np64(inp.get("z")),
+                                 dt_bias=np64(inp["dt_bias"]))
+    check_close(np64(y), yr, *TOL[io], "decode y")
+    check_close(np64(state), sr, *TOL_STATE, "decode state")
