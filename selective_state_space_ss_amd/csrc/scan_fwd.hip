@@ -1,11 +1,11 @@
 // Prompt / prefill selective scan for gfx950.
 //
 // Work decomposition. A channel row (b, c) is owned by one 16-lane DPP row of
-// a wavefront: a wave holds 4 channels of one batch row, a 256-thread block
-// 16 channels. The sequence is walked in chunks of 16*K tokens; inside a
-// chunk lane l of a row owns the K consecutive tokens [l*K, (l+1)*K).
-// Per chunk:
-//   1. each lane loads its K tokens of x, dt (and z), coalesced along seq;
+// a wavefront: a wave holds 4 channels of one batch row, a block of W waves
+// 4W channels of that batch row. The sequence is walked in chunks of 16*K
+// tokens; inside a chunk lane l of a row owns the K consecutive tokens
+// [l*K, (l+1)*K). Per chunk:
+//   1. each lane loads its K tokens of x and dt, coalesced along seq;
 //   2. the block stages the chunk's B and C (shared by all its channels:
 //      one group, nnterp "selective_scan" page) into LDS as fp32;
 //   3. per token: dt = softplus(dt + dt_bias), dt*x, D*x (nnterp page, class
@@ -13,17 +13,23 @@
 //   4. for every state coordinate n:
 //        a_t = exp(dt_t A[c,n]) (0 at a reset token), b_t = dt_t x_t B[n,t];
 //        the lane folds its K pairs from a zero state into (A_l, B_l), with
-//        A_l = exp(A[c,n] * sum dt) (0 if the lane holds a reset);
-//        a 16-lane DPP inclusive scan of (A_l, B_l) under the combine
-//        (a1,b1),(a2,b2) -> (a2 a1, a2 b1 + b2) ("s6_reset" post,
-//        Associative Boundary Resetting) gives each lane the map of all
-//        earlier lanes; applied to the carry from the previous chunk it is
-//        the lane's incoming state; the row total advances the carry;
-//        the lane then walks its K tokens, h = a h + b, y += C[n,t] h;
+//        A_l = exp(A[c,n] * sum dt) (0 if the lane holds a reset); lane 0 of
+//        the row also applies its map to the state carried in from the
+//        previous chunk; a 16-lane DPP inclusive scan of the pairs under
+//        the combine (a1,b1),(a2,b2) -> (a2 a1, a2 b1 + b2) ("s6_reset" post,
+//        Associative Boundary Resetting) then leaves in each lane the state
+//        at the end of its segment; shifted by one lane it is the state the
+//        lane starts from, and lane 15's is the next chunk's carry; the lane
+//        walks its K tokens, h = a h + b, y += C[n,t] h;
 //   5. y = (y + D x) * silu(z), rounded to the I/O type and stored.
 // The per-token state never leaves registers (the hardware-aware point of the
 // "s6_reset" post, Performance Implications). After the last chunk the carry
 // is the final state, written to h_last.
+//
+// The kernel is bound by VALU issue (one exp and five FMA-class operations
+// per token and state coordinate), so its shape is chosen for occupancy: the
+// state coordinates run in a rolled loop that keeps one coordinate's K-token
+// arrays live, and the per-row constants and the carried state sit in LDS.
 #include "ss_device.h"
 #include "ss_launch.h"
 
@@ -35,18 +41,34 @@ namespace {
 
 constexpr int kRowLanes = 16;
 constexpr int kRowsPerWave = 4;
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = 64 * kWavesPerBlock;
-constexpr int kChanPerBlock = kRowsPerWave * kWavesPerBlock;
 
-template <typename IoT, int K, int NMAX, bool GATE, bool RESET>
-__global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams p) {
-  constexpr int T = kRowLanes * K;  // tokens of one chunk of one row
-  constexpr int KP = K + 4;         // LDS stride of one lane's K values (bank spread)
+template <int K, int W>
+struct Shape {
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kChan = kRowsPerWave * W;  // channels per block
+  static constexpr int kT = kRowLanes * K;        // tokens per chunk
+};
+
+// Waves per SIMD the register budget is set for (launch bound). K = 16 with
+// bf16 I/O and no reset mask fits 4 (<= 128 VGPRs); the reset mask and fp32
+// z need more registers and run at 3; K = 32 at 2.
+template <typename IoT, int K, bool RESET>
+constexpr int min_waves_per_simd() {
+  return K == 32 ? 2 : ((RESET || sizeof(IoT) == 4) ? 3 : 4);
+}
+
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET>
+__global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void scan_fwd_kernel(
+    const ScanParams p) {
+  using S = Shape<K, W>;
+  constexpr int T = S::kT;
+  constexpr int KP = K + 4;  // LDS stride of one lane's K values (spreads the banks)
   constexpr int VEC = Io<IoT>::kVec;
   static_assert(K % VEC == 0 && K % 16 == 0, "K must hold whole 16-byte vectors");
   __shared__ float sB[NMAX][kRowLanes][KP];
   __shared__ float sC[NMAX][kRowLanes][KP];
+  __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
+  __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -55,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
   const int tl = lane & 15;
   const int64_t blk = blockIdx.x;
   const int64_t b = blk / p.chan_blocks;
-  const int64_t c_raw = (blk - b * p.chan_blocks) * kChanPerBlock + wave * kRowsPerWave + row;
+  const int64_t c_raw = (blk - b * p.chan_blocks) * S::kChan + wave * kRowsPerWave + row;
   const bool row_ok = c_raw < p.channels;
   const int64_t c = row_ok ? c_raw : p.channels - 1;  // rows past the end compute, never store
   const int N = p.N;
@@ -70,12 +92,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
   const IoT* __restrict__ Cg = static_cast<const IoT*>(p.C) + b * N * L;
   const uint8_t* __restrict__ rg = RESET ? p.reset + b * L : nullptr;
 
-  float a2[NMAX];     // A[c, n] * log2(e)
-  float carry[NMAX];  // state entering the current chunk
-#pragma unroll
-  for (int n = 0; n < NMAX; ++n) {
-    a2[n] = n < N ? p.A[c * N + n] * kLog2e : 0.0f;
-    carry[n] = (n < N && p.h0) ? p.h0[(b * p.channels + c) * N + n] : 0.0f;
+  // Per-row constants and the carried state live in LDS, indexed by the
+  // row's slot; each 16-lane row only touches its own slot, and LDS accesses
+  // of one wave complete in order, so no barrier guards them. Coordinates
+  // n >= N get A2 = 0 and a zero state: they run as the identity.
+  const int slot = (wave * kRowsPerWave + row) * NMAX;
+  if (tl < NMAX) {
+    sA2[slot + tl] = tl < N ? p.A[c * N + tl] * kLog2e : 0.0f;
+    sCarry[slot + tl] = (tl < N && p.h0) ? p.h0[(b * p.channels + c) * N + tl] : 0.0f;
   }
   const float Dc = p.D ? p.D[c] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[c] : 0.0f;
@@ -86,18 +110,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
     const int64_t tb = t0 + tl * K;  // this lane's first token
     const bool full = p.vec_ok && (t0 + T <= L);
 
-    // 1. this lane's tokens
+    // 1. this lane's tokens of x and dt, and z (raw; it is needed only after
+    // the state loop, and loading it here keeps its latency out of the way)
     float xv[K], dv[K];
-    uint32_t zraw[GATE ? (K * sizeof(IoT) / 4) : 1];
+    uint4 zraw[GATE ? K / VEC : 1];
     if (full) {
 #pragma unroll
       for (int v = 0; v < K / VEC; ++v) {
         load_vec16(xg + tb + v * VEC, xv + v * VEC);
         load_vec16(dg + tb + v * VEC, dv + v * VEC);
-        if constexpr (GATE) {
-          const uint4 w = *reinterpret_cast<const uint4*>(zg + tb + v * VEC);
-          zraw[4 * v] = w.x; zraw[4 * v + 1] = w.y; zraw[4 * v + 2] = w.z; zraw[4 * v + 3] = w.w;
-        }
+        if constexpr (GATE) zraw[v] = *reinterpret_cast<const uint4*>(zg + tb + v * VEC);
       }
     } else {
 #pragma unroll
@@ -105,20 +127,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
         const bool in = tb + j < L;
         xv[j] = in ? Io<IoT>::to_f32(xg[tb + j]) : 0.0f;
         dv[j] = in ? Io<IoT>::to_f32(dg[tb + j]) : 0.0f;
-      }
-      if constexpr (GATE) {
-#pragma unroll
-        for (int w = 0; w < (int)(K * sizeof(IoT) / 4); ++w) {
-          if constexpr (sizeof(IoT) == 4) {
-            const bool in = tb + w < L;
-            zraw[w] = in ? __builtin_bit_cast(uint32_t, Io<IoT>::to_f32(zg[tb + w])) : 0u;
-          } else {
-            const bool in0 = tb + 2 * w < L, in1 = tb + 2 * w + 1 < L;
-            const uint32_t lo = in0 ? reinterpret_cast<const uint16_t*>(zg)[tb + 2 * w] : 0u;
-            const uint32_t hi = in1 ? reinterpret_cast<const uint16_t*>(zg)[tb + 2 * w + 1] : 0u;
-            zraw[w] = lo | (hi << 16);
-          }
-        }
       }
     }
     uint32_t rbits = 0;  // bit j: token tb + j starts a document
@@ -139,18 +147,23 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
       }
     }
 
-    // 2. stage this chunk's B and C (fp32) for the whole block
+    // 2. stage this chunk's B and C (fp32) for the whole block. State
+    // coordinates n >= N are staged as zeros: with A2 = 0 they run as the
+    // identity map and add nothing to y, so the n loop needs no bounds check.
     __syncthreads();  // previous chunk's readers are done
     {
       constexpr int kSegPerN = T / VEC;
-      const int nseg = N * kSegPerN;
-      for (int s = tid; s < nseg; s += kThreads) {
+      constexpr int kSeg = NMAX * kSegPerN;
+      for (int s = tid; s < kSeg; s += S::kThreads) {
         const int n = s / kSegPerN;
         const int tpos = (s - n * kSegPerN) * VEC;
         const int sl = tpos / K, sj = tpos - sl * K;
         float vb[VEC], vc[VEC];
         const int64_t g = (int64_t)n * L + t0 + tpos;
-        if (full) {
+        if (n >= N) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) vb[e] = vc[e] = 0.0f;
+        } else if (full) {
           load_vec16(Bg + g, vb);
           load_vec16(Cg + g, vc);
         } else {
@@ -190,61 +203,55 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
       }
     }
 
-    // 4. state coordinates
-#pragma unroll
+    // 4. state coordinates, one per iteration
+#pragma unroll 1
     for (int n = 0; n < NMAX; ++n) {
-      if (n < N) {
-        float av[K], bv[K];
-        const float* bs = &sB[n][tl][0];
+      const float a2n = sA2[slot + n];
+      const float carry = sCarry[slot + n];
+      float av[K], bv[K];
 #pragma unroll
-        for (int j = 0; j < K; j += 4) {
-          const float4 q = *reinterpret_cast<const float4*>(bs + j);
-          const float qq[4] = {q.x, q.y, q.z, q.w};
+      for (int j = 0; j < K; j += 4) {
+        const float4 qb = *reinterpret_cast<const float4*>(&sB[n][tl][j]);
+        bv[j] = qb.x; bv[j + 1] = qb.y; bv[j + 2] = qb.z; bv[j + 3] = qb.w;
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = RESET ? __builtin_fmaf(dtv[j + i], a2[n], mj[j + i]) : dtv[j + i] * a2[n];
-            av[j + i] = fast_exp2(e);
-            bv[j + i] = dtx[j + i] * qq[i];
-          }
-        }
-        float Bl = bv[0];
+      for (int j = 0; j < K; ++j) {
+        const float e = RESET ? __builtin_fmaf(dtv[j], a2n, mj[j]) : dtv[j] * a2n;
+        av[j] = fast_exp2(e);
+        bv[j] *= dtx[j];
+      }
+      float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2n, mlane) : sdt * a2n);
+      // fold from a zero state; lane 0 starts from the carried state instead
+      float Bl = __builtin_fmaf(av[0], tl == 0 ? carry : 0.0f, bv[0]);
 #pragma unroll
-        for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
-        float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2[n], mlane) : sdt * a2[n]);
-        row16_inclusive_scan(Al, Bl);
-        const float Ae = dpp_or<kDppRowShr1>(1.0f, Al);  // exclusive: lanes before this one
-        const float Be = dpp_or<kDppRowShr1>(0.0f, Bl);
-        const float At = dpp_or<kDppRowNewBcast15>(0.0f, Al);  // whole chunk of the row
-        const float Bt = dpp_or<kDppRowNewBcast15>(0.0f, Bl);
-        float h = __builtin_fmaf(Ae, carry[n], Be);
-        carry[n] = __builtin_fmaf(At, carry[n], Bt);
-        const float* cs = &sC[n][tl][0];
+      for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
+      row16_inclusive_scan(Al, Bl);                            // Bl: state after this lane's tokens
+      float h = dpp_or<kDppRowShr1>(carry, Bl);                // state before them
+      sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(0.0f, Bl);  // state after the chunk
 #pragma unroll
-        for (int j = 0; j < K; j += 4) {
-          const float4 q = *reinterpret_cast<const float4*>(cs + j);
-          const float qq[4] = {q.x, q.y, q.z, q.w};
+      for (int j = 0; j < K; j += 4) {
+        const float4 qc = *reinterpret_cast<const float4*>(&sC[n][tl][j]);
+        const float cq[4] = {qc.x, qc.y, qc.z, qc.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            h = __builtin_fmaf(av[j + i], h, bv[j + i]);
-            yv[j + i] = __builtin_fmaf(qq[i], h, yv[j + i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          h = __builtin_fmaf(av[j + i], h, bv[j + i]);
+          yv[j + i] = __builtin_fmaf(cq[i], h, yv[j + i]);
         }
       }
     }
 
     // 5. gate and store
     if constexpr (GATE) {
+      float zv[K];
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        float zf;
-        if constexpr (sizeof(IoT) == 4) {
-          zf = __builtin_bit_cast(float, zraw[j]);
-        } else {
-          const uint32_t w = zraw[j >> 1];
-          zf = __builtin_bit_cast(float, (j & 1) ? (w & 0xffff0000u) : (w << 16));
-        }
-        yv[j] *= silu_f32(zf);
+        for (int v = 0; v < K / VEC; ++v) unpack_vec16<IoT>(zraw[v], zv + v * VEC);
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) zv[j] = tb + j < L ? Io<IoT>::to_f32(zg[tb + j]) : 0.0f;
       }
+#pragma unroll
+      for (int j = 0; j < K; ++j) yv[j] *= silu_f32(zv[j]);
     }
     if (row_ok) {
       if (full) {
@@ -258,30 +265,36 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fwd_kernel(const ScanParams 
     }
   }
 
-  if (p.h_last && row_ok) {
-    float v = 0.0f;
-#pragma unroll
-    for (int n = 0; n < NMAX; ++n) v = (tl == n) ? carry[n] : v;
-    if (tl < N) p.h_last[(b * p.channels + c) * N + tl] = v;
-  }
+  if (p.h_last && row_ok && tl < N) p.h_last[(b * p.channels + c) * N + tl] = sCarry[slot + tl];
 }
 
-template <typename IoT, int K, int NMAX, bool GATE, bool RESET>
-hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET>
+hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
+  ScanParams p = p0;
+  p.chan_blocks = (p.channels + Shape<K, W>::kChan - 1) / Shape<K, W>::kChan;
   const int64_t blocks = p.batch * p.chan_blocks;
-  ScanParams q = p;
-  void* args[] = {&q};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, NMAX, GATE, RESET>),
-                         dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET>),
+                         dim3((unsigned)blocks), dim3(Shape<K, W>::kThreads), args, 0, stream);
 }
 
+// Block shapes. K = 16 tokens per lane keeps a lane's arrays small enough for
+// 4 waves per SIMD (8-wave blocks share one B/C stage); the reset mask's
+// per-token registers leave room for 3, so those blocks have 4 waves. K = 32
+// halves the per-chunk scan overhead at 2 waves per SIMD.
+// SS_SCAN_TOKENS_PER_LANE=16|32 overrides the choice (a tuning knob).
 template <typename IoT, int K, int NMAX>
 hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   const bool gate = p.z != nullptr, reset = p.reset != nullptr;
-  if (gate && reset) return launch_t<IoT, K, NMAX, true, true>(p, stream);
-  if (gate) return launch_t<IoT, K, NMAX, true, false>(p, stream);
-  if (reset) return launch_t<IoT, K, NMAX, false, true>(p, stream);
-  return launch_t<IoT, K, NMAX, false, false>(p, stream);
+  // 8-wave blocks when 4 waves fit per SIMD (two blocks per CU), else 4-wave
+  // blocks (three per CU at 3 waves per SIMD)
+  constexpr int W = min_waves_per_simd<IoT, K, false>() == 4 ? 8 : 4;
+  constexpr int WR = 4;
+  if (gate && reset) return launch_t<IoT, K, WR, NMAX, true, true>(p, stream);
+  if (gate) return launch_t<IoT, K, W, NMAX, true, false>(p, stream);
+  if (reset) return launch_t<IoT, K, WR, NMAX, false, true>(p, stream);
+  return launch_t<IoT, K, W, NMAX, false, false>(p, stream);
 }
 
 template <typename IoT, int K>
@@ -291,33 +304,25 @@ hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   return launch_flags<IoT, K, 16>(p, stream);
 }
 
-// Tokens per lane: 32 halves the per-chunk scan overhead of 16 but nearly
-// fills the 256 VGPRs of a 2-wave/SIMD occupancy; the reset mask and fp32 I/O
-// need more registers than that (they would spill), and short sequences keep
-// 16 so a chunk is not mostly padding.
-// SS_SCAN_TOKENS_PER_LANE=16|32 overrides the choice (a tuning knob).
-int pick_k(const ScanParams& p, bool io_bf16) {
+int pick_k() {
   static const int forced = [] {
     const char* e = std::getenv("SS_SCAN_TOKENS_PER_LANE");
     return e ? std::atoi(e) : 0;
   }();
-  if (forced == 16 || forced == 32) return forced;
-  if (!io_bf16 || p.reset != nullptr) return 16;
-  return p.L >= 16 * 32 ? 32 : 16;
+  return forced == 32 ? 32 : 16;
 }
 
 }  // namespace
 
-hipError_t launch_scan_fwd(const ScanParams& p0, bool io_bf16, hipStream_t stream) {
-  ScanParams p = p0;
-  p.chan_blocks = (p.channels + kChanPerBlock - 1) / kChanPerBlock;
-  const int K = pick_k(p, io_bf16);
+hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream) {
+  const int K = pick_k();
   if (io_bf16) return K == 32 ? launch_n<bf16_t, 32>(p, stream) : launch_n<bf16_t, 16>(p, stream);
   return K == 32 ? launch_n<float, 32>(p, stream) : launch_n<float, 16>(p, stream);
 }
 
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels) {
-  return batch * ((channels + kChanPerBlock - 1) / kChanPerBlock);
+  // the smallest channel block of the instantiations (16 channels)
+  return batch * ((channels + 15) / 16);
 }
 
 }  // namespace ss

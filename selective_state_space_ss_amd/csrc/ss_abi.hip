@@ -1,7 +1,7 @@
 // C ABI entry points: validate, pick the kernel instantiation, enqueue.
 #include <hip/hip_runtime.h>
 
-#include "../../include/ss_scan.h"
+#include "ss_scan.h"
 #include "ss_launch.h"
 #include "ss_validate.h"
 

@@ -50,6 +50,24 @@ __device__ __forceinline__ void load_vec16(const bf16_t* p, float* out) {
   }
 }
 
+// Widen 16 bytes already loaded as raw words.
+template <typename IoT>
+__device__ __forceinline__ void unpack_vec16(const uint4 v, float* out);
+template <>
+__device__ __forceinline__ void unpack_vec16<float>(const uint4 v, float* out) {
+  out[0] = __builtin_bit_cast(float, v.x); out[1] = __builtin_bit_cast(float, v.y);
+  out[2] = __builtin_bit_cast(float, v.z); out[3] = __builtin_bit_cast(float, v.w);
+}
+template <>
+__device__ __forceinline__ void unpack_vec16<bf16_t>(const uint4 v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
 // Narrow and store kVec consecutive elements (16 bytes).
 __device__ __forceinline__ void store_vec16(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);

@@ -4,7 +4,7 @@
 
 #include <stdint.h>
 
-#include "../../include/ss_scan.h"
+#include "ss_scan.h"
 
 namespace ss {
 

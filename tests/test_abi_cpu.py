@@ -107,6 +107,6 @@ def test_validator_header_builds_standalone(tmp_path):
     src = tmp_path / "t.cpp"
     src.write_text('#include "ss_validate.h"\nint main(){ss::ScanArgs a{}; bool n; return ss::validate_scan(a,&n)==SS_ERR_UNSUPPORTED?0:1;}\n')
     exe = tmp_path / "t"
-    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I",
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-I",
                     os.path.join(ROOT, "selective_state_space_ss_amd", "csrc"), str(src), "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
