@@ -65,7 +65,9 @@ int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_d
   p.channels = channels;
   p.N = (int)state_dim;
   p.dt_softplus = dt_softplus != 0;
-  p.vec_ok = state_dim == 16 && vec16(state);
+  const uintptr_t bc_align = io_dtype == SS_BF16 ? 8 : 16;
+  p.vec_ok = state_dim == 16 && vec16(state) && vec16(A) && (reinterpret_cast<uintptr_t>(B) % bc_align) == 0 &&
+             (reinterpret_cast<uintptr_t>(C) % bc_align) == 0;
   p.state = state;
   p.x = x;
   p.dt = dt;

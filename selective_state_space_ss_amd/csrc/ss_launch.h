@@ -32,7 +32,7 @@ struct UpdateParams {
   int64_t batch, channels;
   int N;
   int dt_softplus;
-  int vec_ok;  // state 16-byte aligned and N == 16
+  int vec_ok;  // N == 16, state and A 16-byte aligned, B and C aligned to 4 elements
   float* state;
   const void* x;
   const void* dt;
