@@ -46,7 +46,13 @@ struct UpdateParams {
 };
 
 // io_bf16: element type of x, dt, z, B, C, y (false = float32).
+// launch_scan_fwd picks between the chunked scan (scan_fwd.hip) and the
+// row-parallel walk (scan_rows.hip, launch_scan_rows) by shape.
 hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream);
+hipError_t launch_scan_rows(const ScanParams& p, bool io_bf16, hipStream_t stream);
+// The row-parallel walk needs an even L and x, dt, z, y, B, C (and reset)
+// aligned to two elements.
+bool scan_rows_supported(const ScanParams& p, bool io_bf16);
 hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
 
 }  // namespace ss

@@ -12,13 +12,19 @@ from tests.helpers import TOL, TOL_STATE, check_close, np64, to_dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["chunked", "rows"])
+def scan_kernel(request, monkeypatch):
+    monkeypatch.setenv("SS_SCAN_KERNEL", request.param)
+    return request.param
+
+
 def scan(d, **kw):
     args = dict(D=d["D"], z=d.get("z"), dt_bias=d["dt_bias"], h0=d.get("h0"), reset=d.get("reset"))
     args.update(kw)
     return ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], **args)
 
 
-def test_decode_steps_equal_scan():
+def test_decode_steps_equal_scan(scan_kernel):
     """nnterp "selective_scan" page: the decode call continues from the cached
     state; T decode steps reproduce a T-token scan."""
     d = to_dev(make_case(501, 2, 21, 16, 40, "f32", gate=True, h0=True))
@@ -35,7 +41,7 @@ def test_decode_steps_equal_scan():
 
 
 @pytest.mark.parametrize("L1", [0, 1, 255, 256, 700, 1023])
-def test_split_scan_with_carried_state(L1):
+def test_split_scan_with_carried_state(L1, scan_kernel):
     d = to_dev(make_case(502, 2, 18, 16, 1500, "bf16", gate=True, h0=True, reset_mean_doc=300))
     y, h = scan(d)
     part = lambda t, s, e: None if t is None else t[..., s:e].contiguous()
@@ -51,7 +57,7 @@ def test_split_scan_with_carried_state(L1):
     check_close(np64(h2), np64(h), *TOL_STATE, f"split state at {L1}")
 
 
-def test_packed_row_equals_document_scans():
+def test_packed_row_equals_document_scans(scan_kernel):
     """"s6_reset" post, Sequence Packing: with hard resets a packed row equals
     zero-state scans of its documents."""
     d = to_dev(make_case(503, 1, 20, 16, 1100, "f32", gate=True, h0=True))
@@ -69,7 +75,7 @@ def test_packed_row_equals_document_scans():
     check_close(np64(hd), np64(h), *TOL_STATE, "last document state")
 
 
-def test_deterministic_and_inputs_untouched():
+def test_deterministic_and_inputs_untouched(scan_kernel):
     d = to_dev(make_case(504, 3, 40, 16, 2048, "bf16", gate=True, h0=True, reset_mean_doc=200))
     before = {k: v.clone() for k, v in d.items() if v is not None}
     y1, h1 = scan(d)
@@ -80,7 +86,7 @@ def test_deterministic_and_inputs_untouched():
         assert torch.equal(v, d[k]), f"input {k} was modified"
 
 
-def test_h_last_may_overwrite_h0():
+def test_h_last_may_overwrite_h0(scan_kernel):
     d = to_dev(make_case(505, 2, 33, 16, 700, "bf16", gate=True, h0=True))
     y_ref, h_ref = scan(d)
     h = d["h0"].clone()

@@ -18,6 +18,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
+@pytest.fixture(params=["chunked", "rows"])
+def scan_kernel(request, monkeypatch):
+    """Both prompt-scan kernels (the library picks one by shape; the
+    SS_SCAN_KERNEL override, read at every call, forces one)."""
+    monkeypatch.setenv("SS_SCAN_KERNEL", request.param)
+    return request.param
+
+
 def run_scan(inp, dt_softplus=True, **kw):
     d = to_dev(inp)
     y, h = ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d.get("z"), dt_bias=d["dt_bias"],
@@ -43,10 +51,10 @@ def test_workload_tiny_fp32():
 
 
 @pytest.mark.parametrize("name", ["mamba130m", "mamba2p8b", "packed_reset"])
-def test_workload_full_size_sampled_rows(name):
+def test_workload_full_size_sampled_rows(name, scan_kernel):
     """The full-size launch (the benchmark's), checked on sampled rows."""
     w = WORKLOADS[name]
-    print(f"workload {name} full size", flush=True)
+    print(f"workload {name} full size, {scan_kernel} kernel", flush=True)
     inp = make_inputs(name)
     y, h = run_scan(inp)
     rows = sample_rows(w.batch, w.channels, 40, seed=7)
@@ -84,12 +92,15 @@ RAGGED = [
     ("bf16", 512, True, True, None), ("bf16", 513, True, False, None), ("bf16", 1024, False, True, 64),
     ("bf16", 1543, True, True, None), ("bf16", 2048, True, True, None), ("bf16", 2049, False, False, 100),
     ("bf16", 4100, True, True, 512),
+    # even lengths whose last 16-token tile is partial (the row-parallel walk's tail)
+    ("f32", 2, True, True, None), ("bf16", 14, True, False, 4), ("f32", 18, False, True, 6),
+    ("bf16", 258, True, True, 50), ("bf16", 1030, False, True, None),
 ]
 
 
 @pytest.mark.parametrize("io,L,gate,h0,reset", RAGGED, ids=[f"{r[0]}-L{r[1]}-g{int(r[2])}-h{int(r[3])}-r{r[4]}"
                                                             for r in RAGGED])
-def test_ragged_shapes(io, L, gate, h0, reset):
+def test_ragged_shapes(io, L, gate, h0, reset, scan_kernel):
     """Chunks of 256 or 512 tokens, a ragged tail, channels not a multiple of
     the block's 16."""
     print(f"ragged io={io} L={L} gate={gate} h0={h0} reset={reset}", flush=True)
@@ -99,13 +110,44 @@ def test_ragged_shapes(io, L, gate, h0, reset):
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_state_dims(io, N):
+def test_state_dims(io, N, scan_kernel):
     print(f"state_dim io={io} N={N}", flush=True)
     inp = make_case(200 + N, 3, 5, N, 300, io, gate=True, h0=True, reset_mean_doc=50)
     compare_full(inp, what=f"{io} N={N}")
 
 
-def test_softplus_off_and_optional_inputs_absent():
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_channel_blocks_and_ragged_tail(io, scan_kernel):
+    """Several 64-row blocks with a partial last one, and a partial tile."""
+    print(f"channels=200 io={io}", flush=True)
+    inp = make_case(310, 2, 200, 16, 334, io, gate=True, h0=True, reset_mean_doc=40)
+    compare_full(inp, what=f"{io} channels=200")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_unaligned_inputs(io, scan_kernel):
+    """Tensors that start one element past an aligned address: the library
+    takes its unvectorised paths and the results do not change."""
+    print(f"unaligned io={io}", flush=True)
+    inp = make_case(311, 2, 70, 16, 130, io, gate=True, h0=True, reset_mean_doc=30)
+    compare_full(inp, what=f"{io} aligned")
+    d = to_dev(inp)
+    shifted = {}
+    for k in ("x", "dt", "z", "B", "C"):
+        t = d[k]
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        shifted[k] = v
+    y, h = ss.ss_scan_fwd(shifted["x"], shifted["dt"], d["A"], shifted["B"], shifted["C"], D=d["D"], z=shifted["z"],
+                          dt_bias=d["dt_bias"], h0=d["h0"], reset=d["reset"])
+    torch.cuda.synchronize()
+    yr, hr = oracle_scan_full(inp, True)
+    check_close(np64(y), yr, *TOL[io], f"y unaligned {io}")
+    check_close(np64(h), hr, *TOL_STATE, f"h_last unaligned {io}")
+
+
+def test_softplus_off_and_optional_inputs_absent(scan_kernel):
     inp = make_case(301, 2, 17, 16, 600, "f32", gate=False, h0=False)
     inp["D"] = None
     inp["dt_bias"] = None
@@ -117,7 +159,7 @@ def test_softplus_off_and_optional_inputs_absent():
     check_close(np64(h), hr, *TOL_STATE, "h_last softplus off")
 
 
-def test_seqlen_zero_returns_initial_state():
+def test_seqlen_zero_returns_initial_state(scan_kernel):
     inp = make_case(302, 2, 5, 16, 0, "bf16", gate=True, h0=True)
     y, h = run_scan(inp)
     assert y.numel() == 0
@@ -135,7 +177,7 @@ def test_empty_batch_and_channels_are_noops():
 
 
 # ------------------------------------------------------------------ numerics
-def test_softplus_accuracy():
+def test_softplus_accuracy(scan_kernel):
     """L = 1, N = 1, B = C = x = 1, zero state: y = dt = softplus(dt_raw)."""
     v = torch.linspace(-30, 30, 6001, dtype=torch.float32)
     ch = v.numel()
@@ -146,7 +188,7 @@ def test_softplus_accuracy():
     check_close(np64(y)[0, :, 0], ref, 2e-6, 1e-30, "softplus")
 
 
-def test_gate_accuracy():
+def test_gate_accuracy(scan_kernel):
     """B = 0, D = 1, x = 1: y = silu(z)."""
     z = torch.linspace(-40, 40, 8001, dtype=torch.float32)
     ch = z.numel()
