@@ -8,8 +8,9 @@ A step is one pass of the whole hot path at the Mamba-2.8B layer shape
   * the single-token decode update ss_state_update of a batch-256 cached
     state, in place (workload "decode").
 Inputs are seeded synthetic tensors of those shapes (no trained weights, no
-dataset), resident in HBM before the timed region. W untimed warm-up steps,
-then K timed steps between two device synchronisations.
+dataset), resident in HBM before the timed region. W untimed warm-up steps
+(continued until --warmup-seconds of wall time have passed, so the clocks
+have ramped), then K timed steps between two device synchronisations.
 
 value = whole-step algorithmic bytes / step time (GB/s). The per-kernel
 durations come from HIP events recorded around each launch on the stream the
@@ -57,8 +58,10 @@ COPY_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
@@ -215,9 +218,17 @@ def main():
         torch.cuda.synchronize()
         print("counter pass done", flush=True)
         return
+    # W untimed steps, then more untimed steps until the clocks have ramped
+    # (a cold GPU runs the first few hundred microseconds of work slower)
+    t_w = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    while time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -240,6 +251,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_seconds": round(warm_s, 2),
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
