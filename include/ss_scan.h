@@ -30,7 +30,7 @@
  *  - Inputs are never modified (the decode state excepted). Outputs must not
  *    overlap inputs, except h_last == h0 (same pointer) in the scan and the
  *    in-place state of the decode step.
- *  - state_dim must be in [1, 16]; anything else is SS_ERR_UNSUPPORTED.
+ *  - state_dim must be in [1, 64]; anything else is SS_ERR_UNSUPPORTED.
  *  - Non-finite inputs are outside the contract.
  *  - Results are bitwise identical run to run for the same inputs.
  */
@@ -43,8 +43,8 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 1
-#define SS_MAX_STATE_DIM 16
+#define SS_ABI_VERSION 2
+#define SS_MAX_STATE_DIM 64
 
 typedef enum {
   SS_OK = 0,

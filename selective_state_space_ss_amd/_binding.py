@@ -11,7 +11,7 @@ _LIB_PATH = os.path.join(_PKG, "libssscan.so")
 SS_OK = 0
 SS_F32 = 0
 SS_BF16 = 1
-MAX_STATE_DIM = 16
+MAX_STATE_DIM = 64
 
 _lib = None
 

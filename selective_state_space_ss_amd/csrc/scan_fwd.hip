@@ -66,8 +66,13 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
   constexpr int KP = K + 4;  // LDS stride of one lane's K values (spreads the banks)
   constexpr int VEC = Io<IoT>::kVec;
   static_assert(K % VEC == 0 && K % 16 == 0, "K must hold whole 16-byte vectors");
-  __shared__ float sB[NMAX][kRowLanes][KP];
-  __shared__ float sC[NMAX][kRowLanes][KP];
+  // State coordinates go in groups of NG: a group's B and C are staged in LDS
+  // at a time (one group when NMAX <= 16; LDS holds 16 coordinates' worth).
+  constexpr int NG = NMAX < 16 ? NMAX : 16;
+  constexpr int kGroups = NMAX / NG;
+  static_assert(kGroups * NG == NMAX, "NMAX is a multiple of the group size");
+  __shared__ float sB[NG][kRowLanes][KP];
+  __shared__ float sC[NG][kRowLanes][KP];
   __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
   __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
 
@@ -98,9 +103,9 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
   // of one wave complete in order, so no barrier guards them. Coordinates
   // n >= N get A2 = 0 and a zero state: they run as the identity.
   const int slot = (wave * kRowsPerWave + row) * NMAX;
-  if (tl < NMAX) {
-    sA2[slot + tl] = tl < N ? p.A[c * N + tl] * kLog2e : 0.0f;
-    sCarry[slot + tl] = (tl < N && p.h0) ? p.h0[(b * p.channels + c) * N + tl] : 0.0f;
+  for (int n = tl; n < NMAX; n += kRowLanes) {
+    sA2[slot + n] = n < N ? p.A[c * N + n] * kLog2e : 0.0f;
+    sCarry[slot + n] = (n < N && p.h0) ? p.h0[(b * p.channels + c) * N + n] : 0.0f;
   }
   const float Dc = p.D ? p.D[c] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[c] : 0.0f;
@@ -148,41 +153,47 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
       }
     }
 
-    // 2. stage this chunk's B and C (fp32) for the whole block. State
-    // coordinates n >= N are staged as zeros: with A2 = 0 they run as the
-    // identity map and add nothing to y, so the n loop needs no bounds check.
-    __syncthreads();  // previous chunk's readers are done
-    {
-      constexpr int kSegPerN = T / VEC;
-      constexpr int kSeg = NMAX * kSegPerN;
-      for (int s = tid; s < kSeg; s += S::kThreads) {
-        const int n = s / kSegPerN;
-        const int tpos = (s - n * kSegPerN) * VEC;
-        const int sl = tpos / K, sj = tpos - sl * K;
-        float vb[VEC], vc[VEC];
-        const int64_t g = (int64_t)n * L + t0 + tpos;
-        if (n >= N) {
+    // 2. stage this chunk's B and C (fp32) of a group of coordinates for the
+    // whole block, between two barriers (the first: the previous readers are
+    // done). Coordinates n >= N are staged as zeros: with A2 = 0 they run as
+    // the identity map and add nothing to y, so the n loop needs no bounds
+    // check.
+    auto stage = [&](int grp) {
+      __syncthreads();
+      {
+        constexpr int kSegPerN = T / VEC;
+        constexpr int kSeg = NG * kSegPerN;
+        for (int s = tid; s < kSeg; s += S::kThreads) {
+          const int nl = s / kSegPerN;
+          const int n = grp * NG + nl;
+          const int tpos = (s - nl * kSegPerN) * VEC;
+          const int sl = tpos / K, sj = tpos - sl * K;
+          float vb[VEC], vc[VEC];
+          const int64_t g = (int64_t)n * L + t0 + tpos;
+          if (n >= N) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) vb[e] = vc[e] = 0.0f;
-        } else if (full) {
-          load_vec16(Bg + g, vb);
-          load_vec16(Cg + g, vc);
-        } else {
+            for (int e = 0; e < VEC; ++e) vb[e] = vc[e] = 0.0f;
+          } else if (full) {
+            load_vec16(Bg + g, vb);
+            load_vec16(Cg + g, vc);
+          } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const bool in = t0 + tpos + e < L;
-            vb[e] = in ? Io<IoT>::to_f32(Bg[g + e]) : 0.0f;
-            vc[e] = in ? Io<IoT>::to_f32(Cg[g + e]) : 0.0f;
+            for (int e = 0; e < VEC; ++e) {
+              const bool in = t0 + tpos + e < L;
+              vb[e] = in ? Io<IoT>::to_f32(Bg[g + e]) : 0.0f;
+              vc[e] = in ? Io<IoT>::to_f32(Cg[g + e]) : 0.0f;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) {
+            *reinterpret_cast<float4*>(&sB[nl][sl][sj + e]) = make_float4(vb[e], vb[e + 1], vb[e + 2], vb[e + 3]);
+            *reinterpret_cast<float4*>(&sC[nl][sl][sj + e]) = make_float4(vc[e], vc[e + 1], vc[e + 2], vc[e + 3]);
           }
         }
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-          *reinterpret_cast<float4*>(&sB[n][sl][sj + e]) = make_float4(vb[e], vb[e + 1], vb[e + 2], vb[e + 3]);
-          *reinterpret_cast<float4*>(&sC[n][sl][sj + e]) = make_float4(vc[e], vc[e + 1], vc[e + 2], vc[e + 3]);
-        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
+    };
+    stage(0);
 
     // 3. per-token step size, dt*x, skip term
     float dtv[K], dtx[K], yv[K], mj[RESET ? K : 1];
@@ -204,41 +215,50 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
       }
     }
 
-    // 4. state coordinates, one per iteration
+    // 4. the group's state coordinates, one per iteration
+    auto coords = [&](int grp) {
 #pragma unroll 1
-    for (int n = 0; n < NMAX; ++n) {
-      const float a2n = sA2[slot + n];
-      const float carry = sCarry[slot + n];
-      float av[K], bv[K];
+      for (int nl = 0; nl < NG; ++nl) {
+        const int n = grp * NG + nl;
+        const float a2n = sA2[slot + n];
+        const float carry = sCarry[slot + n];
+        float av[K], bv[K];
 #pragma unroll
-      for (int j = 0; j < K; j += 4) {
-        const float4 qb = *reinterpret_cast<const float4*>(&sB[n][tl][j]);
-        bv[j] = qb.x; bv[j + 1] = qb.y; bv[j + 2] = qb.z; bv[j + 3] = qb.w;
-      }
+        for (int j = 0; j < K; j += 4) {
+          const float4 qb = *reinterpret_cast<const float4*>(&sB[nl][tl][j]);
+          bv[j] = qb.x; bv[j + 1] = qb.y; bv[j + 2] = qb.z; bv[j + 3] = qb.w;
+        }
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const float e = RESET ? __builtin_fmaf(dtv[j], a2n, mj[j]) : dtv[j] * a2n;
-        av[j] = fast_exp2(e);
-        bv[j] *= dtx[j];
-      }
-      float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2n, mlane) : sdt * a2n);
-      // fold from a zero state; lane 0 starts from the carried state instead
-      float Bl = __builtin_fmaf(av[0], tl == 0 ? carry : 0.0f, bv[0]);
+        for (int j = 0; j < K; ++j) {
+          const float e = RESET ? __builtin_fmaf(dtv[j], a2n, mj[j]) : dtv[j] * a2n;
+          av[j] = fast_exp2(e);
+          bv[j] *= dtx[j];
+        }
+        float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2n, mlane) : sdt * a2n);
+        // fold from a zero state; lane 0 starts from the carried state instead
+        float Bl = __builtin_fmaf(av[0], tl == 0 ? carry : 0.0f, bv[0]);
 #pragma unroll
-      for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
-      row16_inclusive_scan(Al, Bl);                            // Bl: state after this lane's tokens
-      float h = dpp_or<kDppRowShr1>(carry, Bl);                // state before them
-      sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(0.0f, Bl);  // state after the chunk
+        for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
+        row16_inclusive_scan(Al, Bl);                            // Bl: state after this lane's tokens
+        float h = dpp_or<kDppRowShr1>(carry, Bl);                // state before them
+        sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(0.0f, Bl);  // state after the chunk
 #pragma unroll
-      for (int j = 0; j < K; j += 4) {
-        const float4 qc = *reinterpret_cast<const float4*>(&sC[n][tl][j]);
-        const float cq[4] = {qc.x, qc.y, qc.z, qc.w};
+        for (int j = 0; j < K; j += 4) {
+          const float4 qc = *reinterpret_cast<const float4*>(&sC[nl][tl][j]);
+          const float cq[4] = {qc.x, qc.y, qc.z, qc.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h = __builtin_fmaf(av[j + i], h, bv[j + i]);
-          yv[j + i] = __builtin_fmaf(cq[i], h, yv[j + i]);
+          for (int i = 0; i < 4; ++i) {
+            h = __builtin_fmaf(av[j + i], h, bv[j + i]);
+            yv[j + i] = __builtin_fmaf(cq[i], h, yv[j + i]);
+          }
         }
       }
+    };
+    coords(0);
+#pragma unroll 1
+    for (int grp = 1; grp < kGroups; ++grp) {
+      stage(grp);
+      coords(grp);
     }
 
     // 5. gate and store
@@ -266,7 +286,8 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     }
   }
 
-  if (p.h_last && row_ok && tl < N) p.h_last[(b * p.channels + c) * N + tl] = sCarry[slot + tl];
+  if (p.h_last && row_ok)
+    for (int n = tl; n < N; n += kRowLanes) p.h_last[(b * p.channels + c) * N + n] = sCarry[slot + n];
 }
 
 template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET>
@@ -298,11 +319,19 @@ hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   return launch_t<IoT, K, W, NMAX, false, false>(p, stream);
 }
 
+// N_max instances: 4, 8, 16, 32, 64 (coordinates past N run as the identity).
+// K = 32 is instantiated up to 16 coordinates only; wider states take K = 16.
 template <typename IoT, int K>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
   if (p.N <= 4) return launch_flags<IoT, K, 4>(p, stream);
   if (p.N <= 8) return launch_flags<IoT, K, 8>(p, stream);
-  return launch_flags<IoT, K, 16>(p, stream);
+  if (p.N <= 16) return launch_flags<IoT, K, 16>(p, stream);
+  if constexpr (K == 16) {
+    if (p.N <= 32) return launch_flags<IoT, K, 32>(p, stream);
+    return launch_flags<IoT, K, 64>(p, stream);
+  } else {
+    return launch_n<IoT, 16>(p, stream);
+  }
 }
 
 int pick_k() {

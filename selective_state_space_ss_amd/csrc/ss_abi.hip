@@ -59,14 +59,14 @@ int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_d
   bool noop = false;
   const ss_status st = ss::validate_update(a, &noop);
   if (st != SS_OK || noop) return st;
-  if (!ss::state_update_grid_ok(batch, channels)) return SS_ERR_SHAPE;
+  if (!ss::state_update_grid_ok(batch, channels, state_dim)) return SS_ERR_SHAPE;
   ss::UpdateParams p{};
   p.batch = batch;
   p.channels = channels;
   p.N = (int)state_dim;
   p.dt_softplus = dt_softplus != 0;
   const uintptr_t bc_align = io_dtype == SS_BF16 ? 8 : 16;
-  p.vec_ok = state_dim == 16 && vec16(state) && vec16(A) && (reinterpret_cast<uintptr_t>(B) % bc_align) == 0 &&
+  p.vec_ok = (state_dim == 16 || state_dim == 32 || state_dim == 64) && vec16(state) && vec16(A) && (reinterpret_cast<uintptr_t>(B) % bc_align) == 0 &&
              (reinterpret_cast<uintptr_t>(C) % bc_align) == 0;
   p.state = state;
   p.x = x;
@@ -88,7 +88,7 @@ const char* ss_status_str(int status) {
     case SS_ERR_NULL: return "SS_ERR_NULL: a required pointer is NULL";
     case SS_ERR_SHAPE: return "SS_ERR_SHAPE: a size is negative or too large";
     case SS_ERR_DTYPE: return "SS_ERR_DTYPE: io_dtype is not SS_F32 or SS_BF16";
-    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 16]";
+    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 64]";
     case SS_ERR_ALIAS: return "SS_ERR_ALIAS: an output overlaps an input";
     case SS_ERR_HIP: return "SS_ERR_HIP: the HIP runtime failed to launch the kernel";
     case SS_ERR_ALIGN: return "SS_ERR_ALIGN: a pointer is not aligned to its element size";

@@ -32,7 +32,7 @@ struct UpdateParams {
   int64_t batch, channels;
   int N;
   int dt_softplus;
-  int vec_ok;  // N == 16, state and A 16-byte aligned, B and C aligned to 4 elements
+  int vec_ok;  // N is 16, 32 or 64, state and A 16-byte aligned, B and C aligned to 4 elements
   float* state;
   const void* x;
   const void* dt;
@@ -60,5 +60,5 @@ hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t 
 namespace ss {
 // Launch-geometry limits, checked by the C ABI before launching.
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
-bool state_update_grid_ok(int64_t batch, int64_t channels);
+bool state_update_grid_ok(int64_t batch, int64_t channels, int64_t state_dim);
 }  // namespace ss

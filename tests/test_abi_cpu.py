@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 1
+    assert ss.abi_version() == 2
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -69,7 +69,7 @@ def test_scan_validation(lib):
     assert scan_call(lib, batch=-1) == SHAPE
     assert scan_call(lib, L=-5) == SHAPE
     assert scan_call(lib, N=0) == UNSUP
-    assert scan_call(lib, N=17) == UNSUP
+    assert scan_call(lib, N=65) == UNSUP
     assert scan_call(lib, x=None) == NULL
     assert scan_call(lib, y=None) == NULL
     assert scan_call(lib, A=None) == NULL
@@ -87,7 +87,7 @@ def test_scan_validation(lib):
 
 def test_update_validation(lib):
     assert upd_call(lib, io=7) == DTYPE
-    assert upd_call(lib, N=17) == UNSUP
+    assert upd_call(lib, N=65) == UNSUP
     assert upd_call(lib, state=None) == NULL
     assert upd_call(lib, y=2 * MB) == ALIAS
     assert upd_call(lib, state=2 * MB) == ALIAS

@@ -101,10 +101,10 @@ def test_c_abi_errors():
     with pytest.raises(ss.SSError) as e:  # y overlapping x
         scan(d, y=d["x"])
     assert e.value.code == 5
-    bad_A = torch.zeros(4, 17, device="cuda")
-    B17 = torch.zeros(1, 17, 64, dtype=torch.bfloat16, device="cuda")
+    bad_A = torch.zeros(4, 65, device="cuda")
+    B65 = torch.zeros(1, 65, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ss.SSError) as e:
-        ss.ss_scan_fwd(d["x"], d["dt"], bad_A, B17, B17)
+        ss.ss_scan_fwd(d["x"], d["dt"], bad_A, B65, B65)
     assert e.value.code == 4
     with pytest.raises(ValueError):
         ss.ss_scan_fwd(d["x"].cpu(), d["dt"], d["A"], d["B"], d["C"])

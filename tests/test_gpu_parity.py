@@ -67,6 +67,15 @@ def test_workload_full_size_sampled_rows(name, scan_kernel):
     assert torch.isfinite(y.float()).all() and torch.isfinite(h).all()
 
 
+@pytest.mark.parametrize("N", [32, 64])
+def test_wide_state_long_sequence(N):
+    """state_dim 32 and 64 over several chunks with a ragged tail: the
+    coordinate groups staged one after another, the carry of each."""
+    print(f"wide state N={N}", flush=True)
+    inp = make_case(320 + N, 2, 40, N, 1100, "bf16", gate=True, h0=True, reset_mean_doc=200)
+    compare_full(inp, what=f"N={N} L=1100")
+
+
 def test_workload_decode_full():
     w = WORKLOADS["decode"]
     print("workload decode", flush=True)
@@ -108,7 +117,7 @@ def test_ragged_shapes(io, L, gate, h0, reset, scan_kernel):
     compare_full(inp, what=f"{io} L={L}")
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17, 24, 31, 32, 33, 48, 63, 64])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_state_dims(io, N, scan_kernel):
     print(f"state_dim io={io} N={N}", flush=True)
@@ -203,7 +212,8 @@ def test_gate_accuracy(scan_kernel):
 
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N,gate", [(1, True), (3, False), (4, True), (9, True), (16, False), (16, True)])
+@pytest.mark.parametrize("N,gate", [(1, True), (3, False), (4, True), (9, True), (16, False), (16, True), (17, True),
+                                    (32, True), (33, False), (48, True), (64, True), (64, False)])
 def test_decode_shapes(io, N, gate):
     print(f"decode io={io} N={N} gate={gate}", flush=True)
     inp = make_decode_case(400 + N, 7, 37, N, io, gate=gate)
