@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--warmup-seconds", type=float, default=1.5,
                     help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extras", action="store_true", help="skip the per-token-states measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
@@ -127,6 +128,41 @@ def recorded_traffic():
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
     return t["traffic_bytes_per_scan"]
+
+
+def measure_states(ss, P, w, scan_bytes: int, stream, reps: int = 20):
+    """ss_scan_fwd_states at the prompt workload's shape, outside the timed
+    step: every token's state ([batch, channels, N, seq] fp32, 4 N bytes per
+    channel-token more to write: bound by HBM) and one selected step (the
+    plain scan's cost). Per-launch HIP-event averages after a warm-up."""
+    import torch
+    ct = w.batch * w.channels * w.seqlen
+    res = {}
+    for label, ts, extra in (("every_token", None, ct * w.state_dim * 4),
+                             ("one_step", w.seqlen // 2, w.batch * w.channels * w.state_dim * 4)):
+        shape = ((w.batch, w.channels, w.state_dim, w.seqlen) if ts is None
+                 else (w.batch, w.channels, w.state_dim))
+        states = torch.empty(shape, dtype=torch.float32, device=P["x"].device)
+        y = torch.empty_like(P["x"])
+        h = torch.empty(w.batch, w.channels, w.state_dim, dtype=torch.float32, device=P["x"].device)
+        f = lambda: ss.ss_scan_fwd_states(P["x"], P["dt"], P["A"], P["B"], P["C"], D=P["D"], z=P["z"],
+                                          dt_bias=P["dt_bias"], h0=P["h0"], time_step=ts, y=y, h_last=h,
+                                          states=states)
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = scan_bytes + extra
+        res[label] = {"us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del states
+    return res
 
 
 def cpu_baseline(inp, w, budget_s: float):
@@ -287,6 +323,8 @@ def main():
                           f"{bytes_p / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f} of 8 TB/s",
         },
     }
+    if not args.no_extras:
+        out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

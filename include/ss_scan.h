@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 2
+#define SS_ABI_VERSION 3
 #define SS_MAX_STATE_DIM 64
 
 typedef enum {
@@ -87,6 +87,33 @@ int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seql
                 const void* x, const void* dt, const float* A, const void* B, const void* C,
                 const float* D, const void* z, const float* dt_bias, const float* h0,
                 const uint8_t* reset, int dt_softplus, void* y, float* h_last, void* stream);
+
+/*
+ * The prompt scan of ss_scan_fwd that also returns states of the recurrence
+ * (nnterp "selective_scan" page: the `states` attribute, the state after
+ * every token of a scan; TransformerLens "ssm_mixer" page: compute_ssm_state,
+ * every step or one selected time_step). Every other argument, output and
+ * convention is that of ss_scan_fwd, and y and h_last are bitwise those of
+ * ss_scan_fwd for the same inputs.
+ *
+ *   states      : output float32, never NULL:
+ *                   time_step < 0: [batch, channels, state_dim, seqlen], the
+ *                     state h_t after every token t, seq fastest like x and
+ *                     y (element [b, c, n, t] is h_t[n] of row (b, c));
+ *                   0 <= time_step < seqlen: [batch, channels, state_dim],
+ *                     the state after token time_step.
+ *                 It must not overlap any input or y / h_last.
+ *   time_step   : see states; time_step >= seqlen is SS_ERR_SHAPE.
+ *
+ * Writing every state moves 4 * state_dim bytes per channel-token to HBM (the
+ * states are 2 * state_dim times the size of a bf16 y), so that form is bound
+ * by HBM bandwidth; the single-step form costs about what ss_scan_fwd does.
+ */
+int ss_scan_fwd_states(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
+                       const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias, const float* h0,
+                       const uint8_t* reset, int dt_softplus, void* y, float* h_last, float* states,
+                       int64_t time_step, void* stream);
 
 /*
  * Single-token decode update of a cached state, in place (nnterp

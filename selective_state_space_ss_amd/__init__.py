@@ -10,6 +10,11 @@ the nnterp "selective_scan" page:
     ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                     dt_softplus=True) -> y          (state updated in place)
 
+and the scan that also returns the state after every token, or after one
+selected token:
+
+    ss_scan_fwd_states(..., time_step=None) -> (y, h_last, states)
+
 Arguments are torch tensors on the GPU: the binding checks them, allocates
 the outputs with torch and passes raw device pointers plus the current HIP
 stream. Every step of the computation runs in the library's kernels; there is
@@ -23,6 +28,7 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     ss_scan_fwd,
+    ss_scan_fwd_states,
     ss_state_update,
     status_str,
 )

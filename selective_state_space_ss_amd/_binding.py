@@ -42,6 +42,8 @@ def load_library() -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.ss_scan_fwd.restype = i32
     lib.ss_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp]
+    lib.ss_scan_fwd_states.restype = i32
+    lib.ss_scan_fwd_states.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp, i64, vp]
     lib.ss_state_update.restype = i32
     lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
     lib.ss_status_str.restype = ctypes.c_char_p
@@ -102,6 +104,43 @@ def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=Non
     False. Preallocated outputs may be passed as y= and h_last= (h_last may be
     h0 itself). Runs on the current torch stream unless stream= is given.
     """
+    y, h_last, args, dev = _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
+                                      return_last_state)
+    rc = load_library().ss_scan_fwd(*args, _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_scan_fwd")
+    return y, h_last
+
+
+def ss_scan_fwd_states(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=None,
+                       dt_softplus: bool = True, *, time_step: Optional[int] = None, y=None, h_last=None,
+                       states=None, stream=None) -> Tuple:
+    """The prompt scan that also returns states: (y, h_last, states), with
+    states [batch, channels, state_dim, seq] (the state after every token, seq
+    fastest like x and y) when time_step is None, else [batch, channels,
+    state_dim] (the state after token time_step). Arguments as ss_scan_fwd;
+    states= takes a preallocated float32 output."""
+    import torch
+    y, h_last, args, dev = _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last, True)
+    batch, channels, L = x.shape
+    N = A.shape[1]
+    ts = -1 if time_step is None else int(time_step)
+    if time_step is not None and ts < 0:
+        raise ValueError("time_step must be None or in [0, seq)")
+    shape = (batch, channels, N, L) if ts < 0 else (batch, channels, N)
+    if states is None:
+        states = torch.empty(shape, dtype=torch.float32, device=dev)
+    else:
+        _check(states, "states", shape, torch.float32, dev)
+    rc = load_library().ss_scan_fwd_states(*args, _ptr(states), ts, _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_scan_fwd_states")
+    return y, h_last, states
+
+
+def _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last, return_last_state):
+    """Check the scan's tensors, allocate missing outputs; returns y, h_last,
+    the C arguments up to h_last, and the device."""
     import torch
     if x.dim() != 3:
         raise ValueError("x must be [batch, channels, seq]")
@@ -139,13 +178,11 @@ def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=Non
         h_last = torch.empty((batch, channels, N), dtype=torch.float32, device=dev)
     elif h_last is not None:
         _check(h_last, "h_last", (batch, channels, N), torch.float32, dev)
-    lib = load_library()
-    rc = lib.ss_scan_fwd(batch, channels, N, L, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                         _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(reset), int(bool(dt_softplus)), _ptr(y),
-                         _ptr(h_last), _stream_handle(dev, stream))
-    if rc != SS_OK:
-        raise SSError(rc, "ss_scan_fwd")
-    return y, h_last
+    args = (batch, channels, N, L, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(dt_bias), _ptr(h0), _ptr(reset), int(bool(dt_softplus)), _ptr(y), _ptr(h_last))
+    return y, h_last, args, dev
+
+
 
 
 def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True, *, y=None,

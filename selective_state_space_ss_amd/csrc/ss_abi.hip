@@ -9,6 +9,51 @@ namespace {
 
 bool vec16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The shared body of ss_scan_fwd and ss_scan_fwd_states (states == nullptr:
+// the plain scan).
+int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, void* stream) {
+  const int64_t batch = a.batch, channels = a.channels, state_dim = a.state_dim, seqlen = a.seqlen;
+  const int io_dtype = a.io_dtype;
+  const void *x = a.x, *dt = a.dt, *z = a.z, *B = a.B, *C = a.C;
+  const uint8_t* reset = a.reset;
+  void* y = a.y;
+  bool noop = false;
+  ss_status st = ss::validate_scan(a, &noop);
+  if (st == SS_OK && states) st = ss::validate_scan_states(a, states, time_step);
+  if (st != SS_OK || noop) return st;
+  if (seqlen == 0 && a.h_last == nullptr) return SS_OK;
+  if (ss::scan_fwd_blocks(batch, channels) > 0x7fffffff) return SS_ERR_SHAPE;
+
+  const bool bf16 = io_dtype == SS_BF16;
+  const int64_t vec = bf16 ? 8 : 4;
+  ss::ScanParams p{};
+  p.batch = batch;
+  p.channels = channels;
+  p.L = seqlen;
+  p.N = (int)state_dim;
+  p.dt_softplus = a.dt_softplus != 0;
+  p.vec_ok = (seqlen % vec == 0) && vec16(x) && vec16(dt) && vec16(z) && vec16(y) && vec16(B) && vec16(C);
+  p.reset_vec = (seqlen % 16 == 0) && vec16(reset);
+  p.x = x;
+  p.dt = dt;
+  p.z = z;
+  p.B = B;
+  p.C = C;
+  p.A = a.A;
+  p.D = a.D;
+  p.dt_bias = a.dt_bias;
+  p.h0 = a.h0;
+  p.reset = reset;
+  p.y = y;
+  p.h_last = a.h_last;
+  p.states = states;
+  p.time_step = time_step;
+  p.states_vec = (seqlen % 4 == 0) && vec16(states);
+  const hipError_t e = states ? ss::launch_scan_states(p, bf16, static_cast<hipStream_t>(stream))
+                              : ss::launch_scan_fwd(p, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -19,36 +64,17 @@ int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seql
                 float* h_last, void* stream) {
   const ss::ScanArgs a{batch, channels, state_dim, seqlen, io_dtype, x,     dt,          A,
                        B,     C,        D,         z,      dt_bias,  h0,    reset, dt_softplus, y, h_last};
-  bool noop = false;
-  const ss_status st = ss::validate_scan(a, &noop);
-  if (st != SS_OK || noop) return st;
-  if (seqlen == 0 && h_last == nullptr) return SS_OK;
-  if (ss::scan_fwd_blocks(batch, channels) > 0x7fffffff) return SS_ERR_SHAPE;
+  return scan_entry(a, nullptr, -1, stream);
+}
 
-  const bool bf16 = io_dtype == SS_BF16;
-  const int64_t vec = bf16 ? 8 : 4;
-  ss::ScanParams p{};
-  p.batch = batch;
-  p.channels = channels;
-  p.L = seqlen;
-  p.N = (int)state_dim;
-  p.dt_softplus = dt_softplus != 0;
-  p.vec_ok = (seqlen % vec == 0) && vec16(x) && vec16(dt) && vec16(z) && vec16(y) && vec16(B) && vec16(C);
-  p.reset_vec = (seqlen % 16 == 0) && vec16(reset);
-  p.x = x;
-  p.dt = dt;
-  p.z = z;
-  p.B = B;
-  p.C = C;
-  p.A = A;
-  p.D = D;
-  p.dt_bias = dt_bias;
-  p.h0 = h0;
-  p.reset = reset;
-  p.y = y;
-  p.h_last = h_last;
-  const hipError_t e = ss::launch_scan_fwd(p, bf16, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+int ss_scan_fwd_states(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
+                       const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const float* dt_bias, const float* h0, const uint8_t* reset, int dt_softplus,
+                       void* y, float* h_last, float* states, int64_t time_step, void* stream) {
+  const ss::ScanArgs a{batch, channels, state_dim, seqlen, io_dtype, x,     dt,          A,
+                       B,     C,        D,         z,      dt_bias,  h0,    reset, dt_softplus, y, h_last};
+  if (!states) return SS_ERR_NULL;
+  return scan_entry(a, states, time_step, stream);
 }
 
 int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_dtype, float* state, const void* x,

@@ -26,6 +26,9 @@ struct ScanParams {
   const uint8_t* reset;
   void* y;
   float* h_last;
+  float* states;      // per-token states (launch_scan_states only)
+  int64_t time_step;  // < 0: every token's state; else the state after this token
+  int states_vec;     // states 16-byte aligned and L a multiple of 4
 };
 
 struct UpdateParams {
@@ -50,6 +53,10 @@ struct UpdateParams {
 // row-parallel walk (scan_rows.hip, launch_scan_rows) by shape.
 hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream);
 hipError_t launch_scan_rows(const ScanParams& p, bool io_bf16, hipStream_t stream);
+// The scan that also writes per-token states (scan_states.hip): p.states
+// receives [batch, channels, N, L] (p.time_step < 0) or the state after token
+// p.time_step, [batch, channels, N].
+hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t stream);
 // The row-parallel walk needs an even L and x, dt, z, y, B, C (and reset)
 // aligned to two elements.
 bool scan_rows_supported(const ScanParams& p, bool io_bf16);

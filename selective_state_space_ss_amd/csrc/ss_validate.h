@@ -89,6 +89,31 @@ inline ss_status validate_scan(const ScanArgs& a, bool* noop) {
   return SS_OK;
 }
 
+// The per-token states output of ss_scan_fwd_states (after validate_scan has
+// accepted the rest): states must be given, time_step below seqlen, and the
+// buffer must not overlap any input or the other outputs.
+inline ss_status validate_scan_states(const ScanArgs& a, const float* states, int64_t time_step) {
+  if (!states) return SS_ERR_NULL;
+  if (time_step >= a.seqlen) return SS_ERR_SHAPE;
+  if (!aligned(states, 4)) return SS_ERR_ALIGN;
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t rows, st, tok, tok_bytes, bc_bytes, a_bytes, rs_bytes, s_bytes;
+  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, a.state_dim, &st) ||
+      !mul_ok(st, time_step < 0 ? a.seqlen : 1, &s_bytes) || !mul_ok(s_bytes, 4, &s_bytes) ||
+      !mul_ok(rows, a.seqlen, &tok) || !mul_ok(tok, es, &tok_bytes) ||
+      !mul_ok(a.batch * a.state_dim, a.seqlen * es, &bc_bytes) || !mul_ok(a.channels * a.state_dim, 4, &a_bytes) ||
+      !mul_ok(a.batch, a.seqlen, &rs_bytes))
+    return SS_ERR_SHAPE;
+  const Span s(states, s_bytes);
+  const Span others[] = {Span(a.x, tok_bytes),      Span(a.dt, tok_bytes),           Span(a.z, tok_bytes),
+                         Span(a.B, bc_bytes),       Span(a.C, bc_bytes),             Span(a.A, a_bytes),
+                         Span(a.D, a.channels * 4), Span(a.dt_bias, a.channels * 4), Span(a.h0, st * 4),
+                         Span(a.reset, rs_bytes),   Span(a.y, tok_bytes),            Span(a.h_last, st * 4)};
+  for (const Span& o : others)
+    if (s.overlaps(o)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
 // Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
 struct UpdateArgs {
   int64_t batch, channels, state_dim;

@@ -31,7 +31,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ss_abi_version", "ss_scan_fwd", "ss_state_update", "ss_status_str"]
+    assert declared_functions() == ["ss_abi_version", "ss_scan_fwd", "ss_scan_fwd_states", "ss_state_update",
+                                    "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 2
+    assert ss.abi_version() == 3
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -83,6 +84,29 @@ def test_scan_validation(lib):
     # empty problems are valid no-ops and never reach the device
     assert scan_call(lib, batch=0) == OK
     assert scan_call(lib, channels=0, x=None, dt=None, B=None, C=None, y=None) == OK
+
+
+def states_call(lib, batch=2, channels=8, N=16, L=64, io=1, x=1 * MB, dt=2 * MB, A=3 * MB, B=4 * MB, C=5 * MB,
+                y=6 * MB, h_last=None, states=8 * MB, time_step=-1):
+    return lib.ss_scan_fwd_states(batch, channels, N, L, io, x, dt, A, B, C, None, None, None, None, None, 1, y,
+                                  h_last, states, time_step, None)
+
+
+def test_scan_states_validation(lib):
+    assert states_call(lib, states=None) == NULL
+    assert states_call(lib, time_step=64) == SHAPE          # past the last token
+    assert states_call(lib, time_step=1 << 40) == SHAPE
+    assert states_call(lib, states=8 * MB + 2) == ALIGN
+    assert states_call(lib, states=6 * MB) == ALIAS          # over y
+    assert states_call(lib, states=1 * MB + 64) == ALIAS     # over x
+    assert states_call(lib, h_last=9 * MB, states=9 * MB) == ALIAS
+    # the checked span is every state (batch*channels*L*N floats) or one step's (batch*channels*N)
+    every, one = 2 * 8 * 64 * 16 * 4, 2 * 8 * 16 * 4
+    assert states_call(lib, states=6 * MB - every + 4) == ALIAS               # its last float is y's first
+    assert states_call(lib, states=6 * MB - one + 4, time_step=5) == ALIAS
+    assert states_call(lib, states=6 * MB - every + 4, time_step=5, batch=1 << 40, channels=1 << 40) == SHAPE
+    assert states_call(lib, io=3) == DTYPE
+    assert states_call(lib, batch=0) == OK                   # an empty problem is a no-op
 
 
 def test_update_validation(lib):
