@@ -51,6 +51,8 @@ def _load():
         lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [ctypes.c_int] + [dp] * 3 + [i64, i64]
         lib.oracle_update.restype = ctypes.c_int
         lib.oracle_update.argtypes = [i64, i64, i64] + [dp] * 9 + [ctypes.c_int, dp, i64, i64]
+        lib.oracle_gated_scan.restype = ctypes.c_int
+        lib.oracle_gated_scan.argtypes = [i64, i64, i64, i64] + [dp] * 7 + [i64, i64]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         _lib = lib
@@ -173,3 +175,37 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
         with ThreadPoolExecutor(len(parts)) as ex:
             list(ex.map(run, parts))
     return y, new_state
+
+
+def gated_scan(q, k, v, gamma, s0=None, threads=None):
+    """Scalar-gated state scan ("Mamba 2 Gated State Scan" problem page):
+    S_t = gamma_t S_{t-1} + k_t v_t^T, y_t = q_t^T S_t, from s0 (zeros if None).
+    q, k: [batch, L, dk]; v: [batch, L, dv]; gamma: [batch, L];
+    s0: [batch, dk, dv]. Returns (y [batch, L, dv], final_state [batch, dk, dv])
+    in fp64. Batch items are split over threads; each is one sequential loop."""
+    lib = _load()
+    q = _f64(q)
+    batch, L, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    k = _f64(k, (batch, L, dk))
+    v = _f64(v, (batch, L, dv))
+    gamma = _f64(gamma, (batch, L))
+    s0 = _f64(s0, (batch, dk, dv))
+    y = np.empty((batch, L, dv), dtype=np.float64)
+    fs = np.empty((batch, dk, dv), dtype=np.float64)
+    if batch == 0:
+        return y, fs
+
+    def run(rng):
+        rc = lib.oracle_gated_scan(batch, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(s0), _ptr(y),
+                                   _ptr(fs), rng[0], rng[1])
+        if rc != 0:
+            raise ValueError(f"oracle_gated_scan rejected its arguments (code {rc})")
+
+    parts = _split_rows(batch, _threads(threads))
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return y, fs

@@ -33,6 +33,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
@@ -135,5 +136,49 @@ int oracle_update(int64_t batch, int64_t channels, int64_t N,
         if (z) yt *= silu(z[r]);
         y[r] = yt;
     }
+    return ORACLE_OK;
+}
+
+/*
+ * Scalar-gated state scan ("Mamba 2 Gated State Scan" problem page,
+ * statement): per batch item a state matrix S of dk x dv numbers,
+ *
+ *   S_t = gamma_t * S_{t-1} + k_t v_t^T
+ *   y_t = q_t^T S_t                       (the output reads the updated state)
+ *
+ * starting from s0 (zeros when s0 is NULL; the page starts every batch state
+ * at zero). Layouts (contiguous, C order):
+ *   q, k  : [batch, L, dk];  v, y : [batch, L, dv];  gamma : [batch, L]
+ *   s0, final_state : [batch, dk, dv]
+ * Batch items b in [b_begin, b_end); each is a sequential token loop.
+ */
+int oracle_gated_scan(int64_t batch, int64_t L, int64_t dk, int64_t dv,
+                      const double* q, const double* k, const double* v, const double* gamma,
+                      const double* s0, double* y, double* final_state,
+                      int64_t b_begin, int64_t b_end) {
+    if (batch < 0 || L < 0 || dk < 1 || dv < 1) return ORACLE_BAD_ARG;
+    if (!q || !k || !v || !gamma || !y) return ORACLE_BAD_ARG;
+    if (b_begin < 0 || b_end > batch || b_begin > b_end) return ORACLE_BAD_ARG;
+    double* S = (double*)malloc((size_t)(dk * dv) * sizeof(double));
+    if (!S) return ORACLE_BAD_ARG;
+    for (int64_t b = b_begin; b < b_end; ++b) {
+        for (int64_t e = 0; e < dk * dv; ++e) S[e] = s0 ? s0[b * dk * dv + e] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double g = gamma[b * L + t];
+            const double* kt = k + (b * L + t) * dk;
+            const double* vt = v + (b * L + t) * dv;
+            const double* qt = q + (b * L + t) * dk;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];
+                y[(b * L + t) * dv + j] = acc;
+            }
+        }
+        if (final_state)
+            for (int64_t e = 0; e < dk * dv; ++e) final_state[b * dk * dv + e] = S[e];
+    }
+    free(S);
     return ORACLE_OK;
 }

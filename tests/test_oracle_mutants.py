@@ -10,6 +10,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_gated_pins as gpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
@@ -33,6 +34,26 @@ MUTANTS = {
     "h0_ignored": ("h[n] = h0 ? h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
     "silu_is_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "decode_no_skip": ("yt += (D ? D[c] : 0.0) * x[r];", "yt += 0.0;"),
+    # scalar-gated state scan
+    "gated_gate_after_write": ("S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];",
+                               "S[i * dv + j] = g * (S[i * dv + j] + kt[i] * vt[j]);"),
+    "gated_y_reads_old_state": ("""            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];
+                y[(b * L + t) * dv + j] = acc;
+            }""", """            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk; ++i) acc += qt[i] * S[i * dv + j];
+                y[(b * L + t) * dv + j] = acc;
+            }
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];"""),
+    "gated_query_is_key": ("acc += qt[i] * S[i * dv + j];", "acc += kt[i] * S[i * dv + j];"),
+    "gated_initial_state_ignored": ("S[e] = s0 ? s0[b * dk * dv + e] : 0.0;", "S[e] = 0.0;"),
+    "gated_gate_of_next_token": ("const double g = gamma[b * L + t];",
+                                 "const double g = gamma[b * L + (t + 1 < L ? t + 1 : t)];"),
 }
 
 
@@ -45,6 +66,17 @@ def _pin_callables():
         if name == "test_pin6_hand_worked_cases":
             for case in pins._hand_cases():
                 calls.append((f"{name}[{case['name']}]", lambda fn=fn, case=case: fn(case)))
+        else:
+            calls.append((name, fn))
+    for name in dir(gpins):
+        if not name.startswith("test_gpin"):
+            continue
+        fn = getattr(gpins, name)
+        if name == "test_gpin5_hand_worked_cases":
+            for case in gpins._hand_cases():
+                calls.append((f"{name}[{case['name']}]", lambda fn=fn, case=case: fn(case)))
+        elif name in ("test_gpin1_unrolled_sum",):
+            calls.append((name, lambda fn=fn: fn(2, True)))
         else:
             calls.append((name, fn))
     return calls
@@ -69,7 +101,7 @@ def test_pins_catch_mutant(mutant, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(old, new, tmp)
         lib = ctypes.CDLL(so)
-        for fn in ("oracle_scan", "oracle_update", "oracle_softplus"):
+        for fn in ("oracle_scan", "oracle_update", "oracle_softplus", "oracle_gated_scan"):
             getattr(lib, fn).restype = getattr(real, fn).restype
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         monkeypatch.setattr(oracle, "_lib", lib)
