@@ -30,7 +30,8 @@
  *  - Inputs are never modified (the decode state excepted). Outputs must not
  *    overlap inputs, except h_last == h0 (same pointer) in the scan and the
  *    in-place state of the decode step.
- *  - state_dim must be in [1, 64]; anything else is SS_ERR_UNSUPPORTED.
+ *  - state_dim must be in [1, 64]; anything else is SS_ERR_UNSUPPORTED (the
+ *    scan and the decode step).
  *  - Non-finite inputs are outside the contract.
  *  - Results are bitwise identical run to run for the same inputs.
  */
@@ -43,15 +44,16 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 3
+#define SS_ABI_VERSION 4
 #define SS_MAX_STATE_DIM 64
+#define SS_MAX_GATED_DK 256
 
 typedef enum {
   SS_OK = 0,
   SS_ERR_NULL = 1,        /* a required pointer is NULL */
   SS_ERR_SHAPE = 2,       /* a size is negative or an index would overflow */
   SS_ERR_DTYPE = 3,       /* io_dtype is not an ss_dtype */
-  SS_ERR_UNSUPPORTED = 4, /* state_dim outside [1, SS_MAX_STATE_DIM] */
+  SS_ERR_UNSUPPORTED = 4, /* state_dim outside [1, SS_MAX_STATE_DIM]; gated scan: dk, dv */
   SS_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap */
   SS_ERR_HIP = 6,         /* the HIP runtime failed to launch the kernel */
   SS_ERR_ALIGN = 7        /* a pointer is not aligned to its element size */
@@ -132,6 +134,42 @@ int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_d
                     const void* x, const void* dt, const float* A, const void* B, const void* C,
                     const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y,
                     void* stream);
+
+/*
+ * Scalar-gated state scan ("Mamba 2 Gated State Scan" problem page,
+ * statement and requirements): per batch item a state S of dk x dv numbers,
+ *
+ *   S_t = gamma_t * S_{t-1} + k_t v_t^T,     y_t = q_t^T S_t
+ *
+ * (the output reads the updated state), computed in fp32 with the state in
+ * fp32, starting from s0 (zeros when s0 is NULL, as the page starts every
+ * batch state).
+ *
+ *   q, k        : [batch, seqlen, dk]   io_dtype
+ *   v           : [batch, seqlen, dv]   io_dtype
+ *   gamma       : [batch, seqlen]       float32, each in [0, 1]
+ *   s0          : [batch, dk, dv]       state_dtype, or NULL (zeros)
+ *   y           : output [batch, seqlen, dv] io_dtype (rounded to nearest even
+ *                 for bf16)
+ *   final_state : output [batch, dk, dv] state_dtype, the state after the
+ *                 last token (s0, or zeros, when seqlen == 0), or NULL. It
+ *                 may be the same pointer as s0.
+ *
+ * The page returns the final state in the dtype of q: state_dtype ==
+ * io_dtype gives that; state_dtype == SS_F32 with bf16 I/O keeps the state
+ * unrounded, so that a sequence cut into calls (final_state passed back as
+ * s0) gives what one call over the whole sequence gives, up to fp32
+ * rounding order.
+ *
+ * dk must be in [1, SS_MAX_GATED_DK] and dv >= 1 (else SS_ERR_UNSUPPORTED).
+ * Tensors are contiguous; callers with strided tensors copy them first.
+ * batch == 0 is a no-op returning SS_OK. Conventions of the other calls hold
+ * (device pointers, asynchronous on `stream`, validation before any launch,
+ * inputs untouched, bitwise reproducible).
+ */
+int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_dtype, int state_dtype,
+                  const void* q, const void* k, const void* v, const float* gamma, const void* s0, void* y,
+                  void* final_state, void* stream);
 
 /* Static, NUL-terminated name of a status code (unknown codes included). */
 const char* ss_status_str(int status);

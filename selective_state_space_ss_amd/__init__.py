@@ -15,6 +15,10 @@ selected token:
 
     ss_scan_fwd_states(..., time_step=None) -> (y, h_last, states)
 
+and the scalar-gated state scan of the "Mamba 2 Gated State Scan" page:
+
+    ss_gated_scan(q, k, v, gamma, s0=None) -> (y, final_state)
+
 Arguments are torch tensors on the GPU: the binding checks them, allocates
 the outputs with torch and passes raw device pointers plus the current HIP
 stream. Every step of the computation runs in the library's kernels; there is
@@ -25,6 +29,7 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     SSError,
     abi_version,
+    ss_gated_scan,
     library_path,
     load_library,
     ss_scan_fwd,

@@ -44,6 +44,8 @@ def load_library() -> ctypes.CDLL:
     lib.ss_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp]
     lib.ss_scan_fwd_states.restype = i32
     lib.ss_scan_fwd_states.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp, i64, vp]
+    lib.ss_gated_scan.restype = i32
+    lib.ss_gated_scan.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 7 + [vp]
     lib.ss_state_update.restype = i32
     lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
     lib.ss_status_str.restype = ctypes.c_char_p
@@ -183,6 +185,60 @@ def _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
     return y, h_last, args, dev
 
 
+
+
+def ss_gated_scan(q, k, v, gamma, s0=None, *, state_dtype=None, y=None, final_state=None,
+                  return_final_state: bool = True, stream=None) -> Tuple:
+    """Scalar-gated state scan on the GPU: S_t = gamma_t S_{t-1} + k_t v_t^T,
+    y_t = q_t^T S_t, in fp32. q, k: [batch, seq, dk]; v: [batch, seq, dv]
+    (float32 or bfloat16, one dtype); gamma: [batch, seq] float32; s0:
+    [batch, dk, dv] in state_dtype, or None (zeros). state_dtype defaults to
+    that of s0 (or of a given final_state), else to q's dtype, as the page
+    returns the final state; float32 keeps a state carried across calls
+    unrounded. Returns (y [batch, seq, dv] in q's dtype,
+    final_state [batch, dk, dv] in state_dtype, or None when
+    return_final_state is False). Strided inputs are copied to contiguous ones
+    first (the library takes contiguous arrays); preallocated outputs may be
+    passed as y= and final_state= (final_state may be s0 itself)."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k must be [batch, seq, dk] and v [batch, seq, dv]")
+    batch, L, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("ss_gated_scan runs on the GPU: q must be a device tensor")
+    io = q.dtype
+    code = _io_code(io)
+    if state_dtype is not None:
+        sdt = state_dtype
+    elif s0 is not None:
+        sdt = s0.dtype
+    elif final_state is not None:
+        sdt = final_state.dtype
+    else:
+        sdt = io
+    scode = _io_code(sdt)
+    q, k, v, gamma = q.contiguous(), k.contiguous(), v.contiguous(), gamma.contiguous()
+    _check(q, "q", (batch, L, dk), io, dev)
+    _check(k, "k", (batch, L, dk), io, dev)
+    _check(v, "v", (batch, L, dv), io, dev)
+    _check(gamma, "gamma", (batch, L), torch.float32, dev)
+    if s0 is not None:
+        _check(s0, "s0", (batch, dk, dv), sdt, dev)
+    if y is None:
+        y = torch.empty((batch, L, dv), dtype=io, device=dev)
+    else:
+        _check(y, "y", (batch, L, dv), io, dev)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((batch, dk, dv), dtype=sdt, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (batch, dk, dv), sdt, dev)
+    rc = load_library().ss_gated_scan(batch, L, dk, dv, code, scode, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(s0),
+                                      _ptr(y), _ptr(final_state), _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_gated_scan")
+    return y, final_state
 
 
 def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True, *, y=None,

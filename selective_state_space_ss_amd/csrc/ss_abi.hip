@@ -108,13 +108,39 @@ int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_d
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
+int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_dtype, int state_dtype,
+                  const void* q, const void* k, const void* v, const float* gamma, const void* s0, void* y,
+                  void* final_state, void* stream) {
+  const ss::GatedArgs a{batch, seqlen, dk, dv, io_dtype, state_dtype, q, k, v, gamma, s0, y, final_state};
+  bool noop = false;
+  const ss_status st = ss::validate_gated(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (seqlen == 0 && final_state == nullptr) return SS_OK;
+  if (ss::gated_scan_blocks(batch, dv) > 0x7fffffff) return SS_ERR_SHAPE;
+  ss::GatedParams p{};
+  p.batch = batch;
+  p.L = seqlen;
+  p.dk = (int)dk;
+  p.dv = dv;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gamma = gamma;
+  p.s0 = s0;
+  p.y = y;
+  p.final_state = final_state;
+  const hipError_t e = ss::launch_gated_scan(p, io_dtype == SS_BF16, state_dtype == SS_BF16,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
 const char* ss_status_str(int status) {
   switch (status) {
     case SS_OK: return "SS_OK";
     case SS_ERR_NULL: return "SS_ERR_NULL: a required pointer is NULL";
     case SS_ERR_SHAPE: return "SS_ERR_SHAPE: a size is negative or too large";
     case SS_ERR_DTYPE: return "SS_ERR_DTYPE: io_dtype is not SS_F32 or SS_BF16";
-    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 64]";
+    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 64] (gated scan: dk outside [1, 256] or dv < 1)";
     case SS_ERR_ALIAS: return "SS_ERR_ALIAS: an output overlaps an input";
     case SS_ERR_HIP: return "SS_ERR_HIP: the HIP runtime failed to launch the kernel";
     case SS_ERR_ALIGN: return "SS_ERR_ALIGN: a pointer is not aligned to its element size";

@@ -48,6 +48,19 @@ struct UpdateParams {
   void* y;
 };
 
+struct GatedParams {
+  int64_t batch, L, dv;
+  int dk;
+  int64_t col_blocks;  // ceil(dv / columns per block)
+  const void* q;       // [batch, L, dk]
+  const void* k;       // [batch, L, dk]
+  const void* v;       // [batch, L, dv]
+  const float* gamma;  // [batch, L]
+  const void* s0;      // [batch, dk, dv] or nullptr, state dtype
+  void* y;             // [batch, L, dv]
+  void* final_state;   // [batch, dk, dv] or nullptr, state dtype
+};
+
 // io_bf16: element type of x, dt, z, B, C, y (false = float32).
 // launch_scan_fwd picks between the chunked scan (scan_fwd.hip) and the
 // row-parallel walk (scan_rows.hip, launch_scan_rows) by shape.
@@ -61,6 +74,9 @@ hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t str
 // aligned to two elements.
 bool scan_rows_supported(const ScanParams& p, bool io_bf16);
 hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
+// The scalar-gated state scan (gated_scan.hip); io_bf16: element type of q, k, v, y.
+// io_bf16: element type of q, k, v, y; state_bf16: that of s0 and final_state.
+hipError_t launch_gated_scan(const GatedParams& p, bool io_bf16, bool state_bf16, hipStream_t stream);
 
 }  // namespace ss
 
@@ -68,4 +84,5 @@ namespace ss {
 // Launch-geometry limits, checked by the C ABI before launching.
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
 bool state_update_grid_ok(int64_t batch, int64_t channels, int64_t state_dim);
+int64_t gated_scan_blocks(int64_t batch, int64_t dv);
 }  // namespace ss

@@ -114,6 +114,57 @@ inline ss_status validate_scan_states(const ScanArgs& a, const float* states, in
   return SS_OK;
 }
 
+// Inputs of the scalar-gated state scan, in ABI order; see ss_gated_scan.
+struct GatedArgs {
+  int64_t batch, seqlen, dk, dv;
+  int io_dtype, state_dtype;
+  const void *q, *k, *v;
+  const float* gamma;
+  const void* s0;
+  void* y;
+  void* final_state;
+};
+
+inline ss_status validate_gated(const GatedArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.state_dtype != SS_F32 && a.state_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.seqlen < 0 || a.dk < 0 || a.dv < 0) return SS_ERR_SHAPE;
+  if (a.dk < 1 || a.dk > SS_MAX_GATED_DK || a.dv < 1) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  const int64_t ses = a.state_dtype == SS_BF16 ? 2 : 4;
+  int64_t bl, qk, qk_bytes, vy, vy_bytes, g_bytes, st, st_bytes;
+  if (!mul_ok(a.batch, a.seqlen, &bl) || !mul_ok(bl, a.dk, &qk) || !mul_ok(qk, es, &qk_bytes) ||
+      !mul_ok(bl, a.dv, &vy) || !mul_ok(vy, es, &vy_bytes) || !mul_ok(bl, 4, &g_bytes) ||
+      !mul_ok(a.batch, a.dk, &st) || !mul_ok(st, a.dv, &st) || !mul_ok(st, ses, &st_bytes))
+    return SS_ERR_SHAPE;
+  if (qk_bytes > (INT64_MAX >> 2) || vy_bytes > (INT64_MAX >> 2) || st_bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  const bool has_tokens = a.seqlen > 0;
+  if (has_tokens && (!a.q || !a.k || !a.v || !a.gamma || !a.y)) return SS_ERR_NULL;
+  const void* io_ptrs[] = {a.q, a.k, a.v, a.y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+  if (a.gamma && !aligned(a.gamma, 4)) return SS_ERR_ALIGN;
+  const void* st_ptrs[] = {a.s0, a.final_state};
+  for (const void* p : st_ptrs)
+    if (p && !aligned(p, ses)) return SS_ERR_ALIGN;
+  const Span q(a.q, has_tokens ? qk_bytes : 0), k(a.k, has_tokens ? qk_bytes : 0), v(a.v, has_tokens ? vy_bytes : 0),
+      g(a.gamma, has_tokens ? g_bytes : 0), s0(a.s0, st_bytes), y(a.y, has_tokens ? vy_bytes : 0),
+      fs(a.final_state, st_bytes);
+  const Span inputs[] = {q, k, v, g, s0};
+  for (const Span& in : inputs) {
+    if (y.overlaps(in)) return SS_ERR_ALIAS;
+    if (&in != &inputs[4] && fs.overlaps(in)) return SS_ERR_ALIAS;
+  }
+  if (fs.overlaps(s0) && a.final_state != a.s0) return SS_ERR_ALIAS;
+  if (y.overlaps(fs)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
 // Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
 struct UpdateArgs {
   int64_t batch, channels, state_dim;

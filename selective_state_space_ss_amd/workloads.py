@@ -22,6 +22,13 @@ bf16 tensors are the fp32 draws rounded to nearest-even by ``Tensor.to``):
 * ``packed_reset``: ``reset[b, 0] = 1`` and ``reset[b, t >= 1]`` i.i.d.
   Bernoulli(1/512), i.e. geometric document lengths with mean 512 (the last
   document of a row is cut by the row's end).
+
+Scalar-gated state scan cases ("Mamba 2 Gated State Scan" page: q, k
+[batch, seq, dk], v [batch, seq, dv], gamma [batch, seq] in [0, 1]), drawn
+in the order q, k, v, gamma, zero mask, s0: ``q, k ~ N(0, dk^-1/2)``,
+``v ~ N(0, 1)``; ``gamma ~ Uniform(0.9, 1)`` ("decay"), ``Uniform(0, 1)``
+("uniform"), or exactly 1 or 0; with ``zero_rate`` each gamma is also set to
+0 with that probability (a state cleared at that token); ``s0 ~ N(0, 1)``.
 """
 from __future__ import annotations
 
@@ -191,3 +198,32 @@ def make_decode_case(seed: int, batch: int, channels: int, state_dim: int, io_dt
     w = Workload("decode_case", batch, channels, state_dim, 0, io_dtype, gate, 1.0, None, "normal", seed,
                  "decode parity case")
     return make_inputs(w)
+
+
+def make_gated_case(seed: int, batch: int, seqlen: int, dk: int, dv: int, io_dtype: str = "bf16",
+                    gamma: str = "decay", zero_rate: float = 0.0, s0: bool = False,
+                    state_dtype: Optional[str] = None, device: str = "cpu") -> Dict[str, Optional[torch.Tensor]]:
+    """A scalar-gated state-scan case (recipe in the module docstring): keys
+    q, k, v (io_dtype), gamma (fp32) and s0 (state_dtype, default io_dtype,
+    or None)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    io = _TORCH_DTYPE[io_dtype]
+    sdt = io if state_dtype is None else _TORCH_DTYPE[state_dtype]
+    q = _normal(gen, (batch, seqlen, dk), std=dk ** -0.5)
+    k = _normal(gen, (batch, seqlen, dk), std=dk ** -0.5)
+    v = _normal(gen, (batch, seqlen, dv))
+    if gamma == "decay":
+        g = 0.9 + 0.1 * torch.rand((batch, seqlen), generator=gen)
+    elif gamma == "uniform":
+        g = torch.rand((batch, seqlen), generator=gen)
+    elif gamma in ("one", "zero"):
+        g = torch.full((batch, seqlen), 1.0 if gamma == "one" else 0.0)
+    else:
+        raise ValueError(f"unknown gamma recipe {gamma!r}")
+    if zero_rate > 0.0:
+        g = torch.where(torch.rand((batch, seqlen), generator=gen) < zero_rate, torch.zeros_like(g), g)
+    st = _normal(gen, (batch, dk, dv)) if s0 else None
+    out = {"q": q.to(io), "k": k.to(io), "v": v.to(io), "gamma": g.to(torch.float32),
+           "s0": None if st is None else st.to(sdt)}
+    return {key: None if t is None else t.to(device) for key, t in out.items()}

@@ -31,8 +31,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ss_abi_version", "ss_scan_fwd", "ss_scan_fwd_states", "ss_state_update",
-                                    "ss_status_str"]
+    assert declared_functions() == ["ss_abi_version", "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_states",
+                                    "ss_state_update", "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 3
+    assert ss.abi_version() == 4
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -107,6 +107,31 @@ def test_scan_states_validation(lib):
     assert states_call(lib, states=6 * MB - every + 4, time_step=5, batch=1 << 40, channels=1 << 40) == SHAPE
     assert states_call(lib, io=3) == DTYPE
     assert states_call(lib, batch=0) == OK                   # an empty problem is a no-op
+
+
+def gated_call(lib, batch=2, L=64, dk=32, dv=16, io=1, sdt=0, q=1 * MB, k=2 * MB, v=3 * MB, gamma=4 * MB, s0=None,
+               y=5 * MB, final_state=None):
+    return lib.ss_gated_scan(batch, L, dk, dv, io, sdt, q, k, v, gamma, s0, y, final_state, None)
+
+
+def test_gated_validation(lib):
+    assert gated_call(lib, io=5) == DTYPE
+    assert gated_call(lib, sdt=2) == DTYPE
+    assert gated_call(lib, s0=6 * MB + 2) == ALIGN                       # fp32 state
+    assert gated_call(lib, sdt=1, s0=6 * MB + 1) == ALIGN                 # bf16 state
+    assert gated_call(lib, L=-1) == SHAPE
+    assert gated_call(lib, dk=0) == UNSUP
+    assert gated_call(lib, dk=257) == UNSUP
+    assert gated_call(lib, dv=0) == UNSUP
+    assert gated_call(lib, q=None) == NULL
+    assert gated_call(lib, gamma=None) == NULL
+    assert gated_call(lib, q=1 * MB + 1) == ALIGN
+    assert gated_call(lib, gamma=4 * MB + 2) == ALIGN
+    assert gated_call(lib, y=1 * MB) == ALIAS                              # y over q
+    assert gated_call(lib, final_state=3 * MB + 4) == ALIAS                # final_state over v
+    assert gated_call(lib, s0=6 * MB, final_state=6 * MB + 4) == ALIAS     # partial overlap with s0
+    assert gated_call(lib, batch=1 << 40, L=1 << 40) == SHAPE
+    assert gated_call(lib, batch=0) == OK
 
 
 def test_update_validation(lib):

@@ -1,0 +1,204 @@
+"""GPU parity of ss_gated_scan, the scalar-gated state scan of the "Mamba 2
+Gated State Scan" problem page (S_t = gamma_t S_{t-1} + k_t v_t^T,
+y_t = q_t^T S_t), against the fp64 oracle on the same seeded inputs.
+
+Tolerance, from the arithmetic. The kernel computes in fp32 (the page asks
+for fp32 intermediates); every output element is a sum of products whose
+magnitudes add up to what the same scan gives on |q|, |k|, |v|, |s0| (all
+weights gamma are >= 0), here called the absolute sum. An fp32 sum of n
+terms errs by at most n u times its absolute sum (u = 2^-24), typically
+sqrt(n) u; n is at most dk + 16 + a few per chunk, so sqrt(n) <= 17 for
+dk <= 256. The bar is
+
+    |gpu - oracle| <= rtol |oracle| + atol + 2^-19 * absolute sum
+
+(2^-19 = 32 u) with rtol, atol the fp32 (1e-4, 1e-5) and bf16 (2e-2, 1e-4)
+pairs of the selective scan; the last term only matters where cancellation
+leaves an element much smaller than its terms. States returned in bf16 are
+held to the bf16 pair."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_ss_amd as ss
+from selective_state_space_ss_amd.workloads import make_gated_case
+from tests.helpers import np64
+
+pytestmark = pytest.mark.gpu
+
+KAPPA = 2.0 ** -19
+TOLS = {torch.float32: (1e-4, 1e-5), torch.bfloat16: (2e-2, 1e-4)}
+
+
+def oracle_run(c):
+    args = [np64(c[k]) for k in ("q", "k", "v", "gamma")]
+    y, fs = oracle.gated_scan(*args, s0=np64(c["s0"]))
+    ya, fa = oracle.gated_scan(*[np.abs(a) for a in args], s0=None if c["s0"] is None else np.abs(np64(c["s0"])))
+    return y, fs, ya, fa
+
+
+def check(got, ref, ref_abs, dtype, what):
+    rtol, atol = TOLS[dtype]
+    g = np64(got)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    bound = rtol * np.abs(ref) + atol + KAPPA * ref_abs
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; worst at {i}: "
+                             f"gpu {g[i]!r} oracle {ref[i]!r} abs-sum {ref_abs[i]!r}")
+
+
+def to_dev(c):
+    return {k: None if t is None else t.cuda() for k, t in c.items()}
+
+
+CASES = [
+    # io, batch, L, dk, dv, gamma, zero_rate, s0
+    ("f32", 1, 1, 1, 1, "decay", 0.0, False),
+    ("f32", 2, 37, 5, 3, "uniform", 0.0, True),
+    ("f32", 3, 100, 64, 16, "decay", 0.02, True),
+    ("bf16", 2, 513, 128, 64, "decay", 0.01, True),
+    ("f32", 2, 300, 130, 17, "uniform", 0.05, False),
+    ("bf16", 1, 257, 192, 100, "decay", 0.0, True),
+    ("f32", 1, 200, 256, 33, "decay", 0.0, True),
+    ("bf16", 2, 64, 256, 256, "uniform", 0.0, False),
+    ("f32", 2, 16, 100, 64, "one", 0.0, True),
+    ("f32", 1, 600, 64, 64, "one", 0.0, True),
+    ("bf16", 2, 50, 64, 32, "zero", 0.0, True),
+    ("bf16", 4, 1000, 17, 129, "decay", 0.003, False),
+]
+
+
+@pytest.mark.parametrize("io,batch,L,dk,dv,gamma,zero_rate,s0", CASES,
+                         ids=[f"{c[0]}-b{c[1]}-L{c[2]}-dk{c[3]}-dv{c[4]}-{c[5]}" for c in CASES])
+def test_gated_parity(io, batch, L, dk, dv, gamma, zero_rate, s0):
+    print(f"gated io={io} b={batch} L={L} dk={dk} dv={dv} gamma={gamma}", flush=True)
+    c = make_gated_case(900 + L + dk + dv, batch, L, dk, dv, io, gamma=gamma, zero_rate=zero_rate, s0=s0,
+                        state_dtype="f32")
+    d = to_dev(c)
+    y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"], state_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yr, fr, ya, fa = oracle_run(c)
+    assert y.dtype == d["q"].dtype and fs.dtype == torch.float32
+    check(y, yr, ya, y.dtype, "y")
+    check(fs, fr, fa, torch.float32, "final_state")
+
+
+@pytest.mark.parametrize("io,state", [("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"), ("bf16", "f32")])
+def test_state_dtypes(io, state):
+    """The page's default returns the final state in q's dtype; either state
+    dtype is accepted for s0 and final_state with either I/O dtype."""
+    print(f"gated state dtype io={io} state={state}", flush=True)
+    c = make_gated_case(950, 2, 70, 48, 40, io, s0=True, state_dtype=state)
+    d = to_dev(c)
+    y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"], state_dtype=d["s0"].dtype)
+    torch.cuda.synchronize()
+    yr, fr, ya, fa = oracle_run(c)
+    assert fs.dtype == d["s0"].dtype
+    check(y, yr, ya, y.dtype, "y")
+    check(fs, fr, fa, fs.dtype, "final_state")
+    if state == io:   # default state dtype is q's
+        y2, fs2 = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"])
+        torch.cuda.synchronize()
+        assert fs2.dtype == d["q"].dtype and torch.equal(fs2, fs) and torch.equal(y2, y)
+
+
+def test_page_default_zero_state():
+    """No s0: every batch state starts at zero, as the page has it."""
+    print("gated zero state", flush=True)
+    c = make_gated_case(951, 3, 45, 32, 24, "bf16")
+    d = to_dev(c)
+    y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"])
+    torch.cuda.synchronize()
+    yr, fr, ya, fa = oracle_run(c)
+    assert fs.dtype == torch.bfloat16
+    check(y, yr, ya, torch.bfloat16, "y")
+    check(fs, fr, fa, torch.bfloat16, "final_state")
+
+
+def test_in_place_and_chained():
+    """final_state written over s0, and a sequence cut into two calls with an
+    fp32 state carried between them, against one oracle pass over all of it."""
+    print("gated chained", flush=True)
+    c = make_gated_case(952, 2, 700, 128, 64, "bf16", s0=True, state_dtype="f32", zero_rate=0.002)
+    d = to_dev(c)
+    st = d["s0"].clone()
+    y1, f1 = ss.ss_gated_scan(d["q"][:, :300], d["k"][:, :300], d["v"][:, :300], d["gamma"][:, :300], st,
+                              final_state=st)
+    y2, f2 = ss.ss_gated_scan(d["q"][:, 300:], d["k"][:, 300:], d["v"][:, 300:], d["gamma"][:, 300:], st,
+                              final_state=st)
+    torch.cuda.synchronize()
+    assert f1.data_ptr() == st.data_ptr() and f2.data_ptr() == st.data_ptr()
+    yr, fr, ya, fa = oracle_run(c)
+    check(torch.cat([y1, y2], 1), yr, ya, torch.bfloat16, "y")
+    check(st, fr, fa, torch.float32, "final_state")
+
+
+def test_empty_sequence():
+    print("gated empty", flush=True)
+    c = make_gated_case(953, 2, 0, 20, 12, "f32", s0=True)
+    d = to_dev(c)
+    y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"])
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 12)
+    assert torch.equal(fs, d["s0"])
+    y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"])
+    torch.cuda.synchronize()
+    assert torch.equal(fs, torch.zeros_like(fs))
+
+
+def test_noncontiguous_inputs_untouched_and_reproducible():
+    """The page allows noncontiguous inputs and forbids modifying them; two
+    calls give the same bits."""
+    print("gated noncontiguous", flush=True)
+    c = make_gated_case(954, 3, 90, 40, 36, "f32", s0=True)
+    d = to_dev(c)
+    # strided views of the same values
+    qt = d["q"].transpose(1, 2).contiguous().transpose(1, 2)
+    kt = d["k"].transpose(0, 1).contiguous().transpose(0, 1)
+    vt = torch.empty(3, 90, 72, device="cuda")[:, :, ::2]
+    vt.copy_(d["v"])
+    gt = torch.empty(90, 3, device="cuda").t()
+    gt.copy_(d["gamma"])
+    assert not (qt.is_contiguous() or kt.is_contiguous() or vt.is_contiguous() or gt.is_contiguous())
+    before = [t.clone() for t in (qt, kt, vt, gt, d["s0"])]
+    y, fs = ss.ss_gated_scan(qt, kt, vt, gt, d["s0"])
+    y2, fs2 = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"])
+    torch.cuda.synchronize()
+    for a, b in zip((qt, kt, vt, gt, d["s0"]), before):
+        assert torch.equal(a, b), "an input was modified"
+    assert torch.equal(y, y2) and torch.equal(fs, fs2)
+    yr, fr, ya, fa = oracle_run(c)
+    check(y, yr, ya, torch.float32, "y")
+    check(fs, fr, fa, torch.float32, "final_state")
+
+
+def test_errors():
+    c = to_dev(make_gated_case(955, 1, 8, 257, 8, "f32"))
+    with pytest.raises(ss.SSError) as e:
+        ss.ss_gated_scan(c["q"], c["k"], c["v"], c["gamma"])
+    assert e.value.code == 4
+    c = to_dev(make_gated_case(956, 1, 8, 16, 8, "f32"))
+    with pytest.raises(ss.SSError) as e:    # y over q
+        ss.ss_gated_scan(c["q"], c["k"], c["v"], c["gamma"], y=c["q"].view(-1)[:64].view(1, 8, 8))
+    assert e.value.code == 5
+
+
+def test_full_size_sampled():
+    """Batch x heads 640, seq 2048, dk 128, dv 64 (a Mamba-2 2.7B-shaped layer
+    at batch 8: 80 heads of width 64, state 128) in bf16; batch items are
+    independent, so sampled items are checked against the oracle run on their
+    own slices."""
+    print("gated full size 640x2048x128x64", flush=True)
+    c = make_gated_case(957, 640, 2048, 128, 64, "bf16", state_dtype="f32", device="cuda")
+    y, fs = ss.ss_gated_scan(c["q"], c["k"], c["v"], c["gamma"], state_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in (0, 1, 317, 639):
+        sl = {k: None if t is None else t[b:b + 1].cpu() for k, t in c.items()}
+        yr, fr, ya, fa = oracle_run(sl)
+        check(y[b:b + 1], yr, ya, torch.bfloat16, f"y[{b}]")
+        check(fs[b:b + 1], fr, fa, torch.float32, f"final_state[{b}]")
