@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--warmup-seconds", type=float, default=1.5,
                     help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-extras", action="store_true", help="skip the per-token-states measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-token-states and gated-scan measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
@@ -163,6 +164,50 @@ def measure_states(ss, P, w, scan_bytes: int, stream, reps: int = 20):
                       "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del states
     return res
+
+
+GATED_SHAPE = (640, 2048, 128, 64)   # batch x heads, seq, dk, dv
+
+
+def gated_work(batch, L, dk, dv, es):
+    """Algorithmic bytes (q, k, v, y in the I/O dtype, gamma and the fp32
+    final state) and matrix-core flops of one scalar-gated scan launch. The
+    flops are those of the chunked form over 16-token chunks, per token:
+    q.k over the chunk (2 * 16 dk), the weighted sum of v (2 * 16 dv), q^T S
+    (2 dk dv) and the state update (2 dk dv)."""
+    tok = batch * L
+    nbytes = tok * (2 * dk + 2 * dv) * es + tok * 4 + batch * dk * dv * 4
+    flops = tok * (32.0 * dk + 32.0 * dv + 4.0 * dk * dv)
+    return nbytes, flops
+
+
+def measure_gated(ss, stream, reps: int = 20):
+    """ss_gated_scan at batch x heads 640, seq 2048, dk 128, dv 64, bf16 I/O,
+    fp32 final state (a Mamba-2 2.7B-shaped layer at batch 8: 80 heads of
+    width 64, state 128). Per-launch HIP-event average after a warm-up."""
+    import torch
+    from selective_state_space_ss_amd.workloads import make_gated_case
+    batch, L, dk, dv = GATED_SHAPE
+    c = make_gated_case(1010, batch, L, dk, dv, "bf16", device="cuda")
+    y = torch.empty(batch, L, dv, dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty(batch, dk, dv, dtype=torch.float32, device="cuda")
+    f = lambda: ss.ss_gated_scan(c["q"], c["k"], c["v"], c["gamma"], y=y, final_state=fs)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes, flops = gated_work(batch, L, dk, dv, 2)
+    tf = flops / (us * 1e-6) / 1e12
+    return {"shape": {"batch_x_heads": batch, "seq": L, "dk": dk, "dv": dv, "io": "bf16", "state": "f32"},
+            "us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "mfma_flops": flops,
+            "TFLOP_s": round(tf, 2), "mfma_fp32_frac": round(tf / PEAK_FP32_TFLOPS, 4)}
 
 
 def cpu_baseline(inp, w, budget_s: float):
@@ -324,7 +369,8 @@ def main():
         },
     }
     if not args.no_extras:
-        out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream)}
+        out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream),
+                         "ss_gated_scan": measure_gated(ss, stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -16,19 +16,22 @@
 // which is the recurrence unrolled over the chunk (the page's S_t written out
 // from S_prev). Every product is a 16 x 16 x 4 fp32 MFMA.
 //
-// Layout. A block is one batch item and 16 columns of dv, 4 waves; wave w
-// owns rows [w R, (w + 1) R) of dk (R = dk padded to 64, over 4) and keeps
-// its rows of S in registers in the MFMA accumulator layout. Per chunk the
-// block stages q, k (also transposed), v^T and gamma in LDS and builds P and
-// L; each wave then computes, over its own rows, the partial
-//   A^T = K Q^T,  M = A o L,  Y = M V + diag(P) Q S_prev,
-//   S  <- P_15 S + (K o L[15])^T V,
-// and the block sums the 4 partial Y (A, hence M and Y, are linear in the
-// rows of dk they run over). Operands are read from LDS as float4 runs: in
-// the MFMA of step g, lane group G of the wave supplies the contraction index
-// 4G + g (any bijection of the contraction index serves, if A and B operands
-// use the same one), which also makes the accumulator of A^T, register r at
-// lane (t, G), exactly the A operand M[t][4G + r] of the next product.
+// Layout. A block is one batch item and 64 columns of dv, 4 waves of 16
+// columns each; a wave keeps all dk rows of its columns of S in registers, in
+// the MFMA accumulator layout: register r of tile rt at lane (c, G) (c = lane
+// mod 16, G = lane / 16) is S[16 rt + 4 G + r][column c]. That is also the B
+// operand of q^T S_prev when the contraction slot of step g is row
+// 16 rt + 4 G + g, so the state never leaves registers. Each wave forms the
+// 16 x 16 token-token product q k^T over all of dk itself (no exchange
+// between waves).
+//
+// Staging. The block stages a chunk in LDS, double buffered with one barrier
+// per chunk: q and k row-major (operands of q k^T and q S), and k and v in
+// 4-token groups [t / 4][row][t % 4] (the operands that contract over tokens
+// need 4 consecutive tokens of one row per lane), plus L and P. The next
+// chunk's q, k, v are loaded into registers with 16-byte loads, and its gamma
+// into scalar registers, while the current chunk is computed. Inputs whose
+// rows are not whole 16-byte vectors take a slower element-wise path.
 //
 // Rows of dk past dk, columns past dv and tokens past L are staged as zeros
 // (gamma as 1): they change nothing and are never stored.
@@ -39,162 +42,259 @@ namespace ss {
 namespace {
 
 constexpr int kT = 16;     // tokens per chunk
-constexpr int kCols = 16;  // columns of dv per block
 constexpr int kWaves = 4;
+constexpr int kCols = 16 * kWaves;  // columns of dv per block
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTS = kT + 4;  // LDS stride of the [row][token] arrays
+constexpr int kLS = kT + 4;  // LDS stride of L[t][s]
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename IoT, typename StT, int RT>
+// Four consecutive staged elements, widened to fp32.
+__device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+__device__ __forceinline__ v4f ld4(const bf16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return v4f{__builtin_bit_cast(float, w.x << 16), __builtin_bit_cast(float, w.x & 0xffff0000u),
+             __builtin_bit_cast(float, w.y << 16), __builtin_bit_cast(float, w.y & 0xffff0000u)};
+}
+
+template <typename E>
+__device__ __forceinline__ E zero_elem() {
+  if constexpr (sizeof(E) == 2) return bf16_t{0};
+  else return 0.0f;
+}
+
+// Element e of a 16-byte vector of E held as raw words. The element is
+// copied to a scalar before any bit cast: hipcc's __builtin_bit_cast of a
+// vector-element lvalue reads element 0 whatever the index.
+template <typename E>
+__device__ __forceinline__ E elem(const u32x4 v, int e) {
+  if constexpr (sizeof(E) == 2) {
+    const uint32_t w = v[e >> 1];
+    return bf16_t{static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu))};
+  } else {
+    const uint32_t w = v[e];
+    return __builtin_bit_cast(float, w);
+  }
+}
+
+// A block-uniform pointer as a constant-address-space pointer, so that loads
+// through it at uniform indices are scalar loads.
+__device__ __forceinline__ const __attribute__((address_space(4))) float* uniform_f32(const float* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return (const __attribute__((address_space(4))) float*)((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <typename E, int RT>
+struct Stage {
+  static constexpr int DKP = 16 * RT;                     // dk padded
+  static constexpr int QS = DKP + 32 / (int)sizeof(E);    // row stride of q, k
+  static constexpr int KGS = 4 * DKP + 64;                // group stride of the grouped k
+  static constexpr int VGS = 4 * kCols + 64;              // group stride of the grouped v
+  E q[kT][QS];
+  E k[kT][QS];
+  E kg[4 * KGS];  // k[t][i] at [t / 4][i][t % 4]
+  E vg[4 * VGS];  // v[t][j] at [t / 4][j][t % 4]
+  float L[kT][kLS];
+  float P[kT];
+};
+
+template <typename IoT, typename StT, int RT, bool VEC>
 __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams p) {
-  constexpr int R = 16 * RT;        // dk rows per wave
-  constexpr int DKP = kWaves * R;   // dk padded
-  constexpr int QS = DKP + 4;       // LDS stride of the [token][dk] and [column][dk] arrays
-  __shared__ __align__(16) float sQ[kT][QS];         // q[t][i]
-  __shared__ __align__(16) float sK[kT][QS];         // k[s][i]
-  __shared__ __align__(16) float sKT[DKP][kTS];      // k[s][i] at [i][s]
-  __shared__ __align__(16) float sVT[kCols][kTS];    // v[s][j] at [j][s]
-  __shared__ __align__(16) float sL[kT][kTS];        // L[t][s]
-  __shared__ float sG[kT];                           // gamma of the chunk's tokens
-  __shared__ __align__(16) float sP[kT];             // P[t]
-  __shared__ __align__(16) float sST[kCols][QS];     // S_prev[i][j] at [j][i]
-  __shared__ __align__(16) float sYT[kWaves][kCols][kTS];  // partial y[t][j] at [w][j][t]
+  using St = Stage<IoT, RT>;
+  constexpr int DKP = St::DKP;
+  constexpr int VEC_E = 16 / sizeof(IoT);            // elements per 16-byte vector
+  constexpr int QV = kT * DKP / VEC_E;               // vectors per chunk of q (and of k)
+  constexpr int NQV = (QV + kThreads - 1) / kThreads;
+  constexpr int VV = kT * kCols / VEC_E;             // vectors per chunk of v
+  static_assert(VV <= kThreads, "one v vector per thread");
+  static_assert(DKP % VEC_E == 0, "whole vectors per staged row");
+  __shared__ __align__(16) St stage[2];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
-  const int G = l >> 4;   // lane group: the MFMA's contraction slot
+  const int G = l >> 4;
   const int c16 = l & 15;
-  const int64_t blk = blockIdx.x;
-  const int64_t b = blk / p.col_blocks;
-  const int64_t j0 = (blk - b * p.col_blocks) * kCols;
+  const int64_t col_blocks = p.col_blocks;
+  const int64_t b = blockIdx.x / col_blocks;
+  const int64_t jb = (blockIdx.x - b * col_blocks) * kCols;  // block's first column
   const int64_t L = p.L;
   const int dk = p.dk;
   const int64_t dv = p.dv;
-  const int i0w = w * R;  // this wave's first row of dk
   const IoT* __restrict__ qg = static_cast<const IoT*>(p.q) + b * L * dk;
-  const IoT* __restrict__ kg = static_cast<const IoT*>(p.k) + b * L * dk;
-  const IoT* __restrict__ vg = static_cast<const IoT*>(p.v) + b * L * dv;
+  const IoT* __restrict__ kgp = static_cast<const IoT*>(p.k) + b * L * dk;
+  const IoT* __restrict__ vgp = static_cast<const IoT*>(p.v) + b * L * dv;
   const float* __restrict__ gg = p.gamma + b * L;
+  const int64_t jw = jb + 16 * w;       // this wave's first column
+  const int64_t jc = jw + c16;          // this lane's column
+  const bool wave_live = jw < dv;
 
-  // This wave's rows of the state: S[rt][r] = S[i0w + 16 rt + 4 G + r][j0 + c16].
   v4f S[RT];
-  const int64_t jg = j0 + c16;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i0w + 16 * rt + 4 * G + r;
-      S[rt][r] = (p.s0 && i < dk && jg < dv) ? Io<StT>::to_f32(static_cast<const StT*>(p.s0)[(b * dk + i) * dv + jg])
-                                             : 0.0f;
+      const int i = 16 * rt + 4 * G + r;
+      S[rt][r] = (p.s0 && i < dk && jc < dv)
+                     ? Io<StT>::to_f32(static_cast<const StT*>(p.s0)[(b * dk + i) * dv + jc])
+                     : 0.0f;
     }
-  auto publish_state = [&]() {  // S -> sST (this wave's rows only)
+
+  // ---- the next chunk, in registers (q, k, v: vector path only)
+  u32x4 qr[NQV], kr[NQV], vr;
+  float gam[kT];
+  auto prefetch = [&](int64_t t0) {
+    if constexpr (VEC) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      *reinterpret_cast<v4f*>(&sST[c16][i0w + 16 * rt + 4 * G]) = S[rt];
+      for (int n = 0; n < NQV; ++n) {
+        const int e = tid + n * kThreads;
+        const int t = e / (DKP / VEC_E);
+        const int i = (e - t * (DKP / VEC_E)) * VEC_E;
+        const bool in = e < QV && t0 + t < L && i < dk;
+        const int64_t off = (t0 + t) * dk + i;
+        qr[n] = in ? *reinterpret_cast<const u32x4*>(qg + off) : u32x4{0, 0, 0, 0};
+        kr[n] = in ? *reinterpret_cast<const u32x4*>(kgp + off) : u32x4{0, 0, 0, 0};
+      }
+      {
+        const int t = tid / (kCols / VEC_E);
+        const int j = (tid - t * (kCols / VEC_E)) * VEC_E;
+        const bool in = tid < VV && t0 + t < L && jb + j < dv;
+        vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 + t) * dv + jb + j) : u32x4{0, 0, 0, 0};
+      }
+    }
+    // one load per token at a clamped index and a select (tokens past L
+    // read gamma 1): no branch, so every value reaches its use directly
+    const auto* gp = uniform_f32(gg);
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      const bool in = t0 + u < L;
+      const float g = gp[in ? t0 + u : L - 1];
+      gam[u] = in ? g : 1.0f;
+    }
   };
-  publish_state();
+
+  auto write_stage = [&](St& s, int64_t t0) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int n = 0; n < NQV; ++n) {
+        const int e = tid + n * kThreads;
+        if (e < QV) {
+          const int t = e / (DKP / VEC_E);
+          const int i = (e - t * (DKP / VEC_E)) * VEC_E;
+          *reinterpret_cast<u32x4*>(&s.q[t][i]) = qr[n];
+          *reinterpret_cast<u32x4*>(&s.k[t][i]) = kr[n];
+#pragma unroll
+          for (int x = 0; x < VEC_E; ++x) s.kg[(t >> 2) * St::KGS + (i + x) * 4 + (t & 3)] = elem<IoT>(kr[n], x);
+        }
+      }
+      if (tid < VV) {
+        const int t = tid / (kCols / VEC_E);
+        const int j = (tid - t * (kCols / VEC_E)) * VEC_E;
+#pragma unroll
+        for (int x = 0; x < VEC_E; ++x) s.vg[(t >> 2) * St::VGS + (j + x) * 4 + (t & 3)] = elem<IoT>(vr, x);
+      }
+    } else {
+      for (int e = tid; e < kT * DKP; e += kThreads) {
+        const int t = e / DKP, i = e - t * DKP;
+        const bool in = t0 + t < L && i < dk;
+        const IoT qv = in ? qg[(t0 + t) * dk + i] : zero_elem<IoT>();
+        const IoT kv = in ? kgp[(t0 + t) * dk + i] : zero_elem<IoT>();
+        s.q[t][i] = qv;
+        s.k[t][i] = kv;
+        s.kg[(t >> 2) * St::KGS + i * 4 + (t & 3)] = kv;
+      }
+      for (int e = tid; e < kT * kCols; e += kThreads) {
+        const int t = e / kCols, j = e - t * kCols;
+        const bool in = t0 + t < L && jb + j < dv;
+        s.vg[(t >> 2) * St::VGS + j * 4 + (t & 3)] = in ? vgp[(t0 + t) * dv + jb + j] : zero_elem<IoT>();
+      }
+    }
+    // L[t][s] = gamma_{s+1} ... gamma_t (s <= t), P[t] = gamma_0 L[t][0]
+    {
+      const int t = tid >> 4, sidx = tid & 15;
+      float prod = 1.0f;
+#pragma unroll
+      for (int u = 1; u < kT; ++u) prod *= (u > sidx && u <= t) ? gam[u] : 1.0f;
+      s.L[t][sidx] = sidx <= t ? prod : 0.0f;
+      if (sidx == 0) s.P[t] = gam[0] * prod;
+    }
+  };
 
   const int64_t nchunks = (L + kT - 1) / kT;
+  if (nchunks > 0) prefetch(0);
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t t0 = ch * kT;
+    St& s = stage[ch & 1];
+    write_stage(s, t0);
+    __syncthreads();
+    if (ch + 1 < nchunks) prefetch(t0 + kT);
+    if (!wave_live) continue;
 
-    // 1. stage the chunk (the previous chunk's readers are done first)
-    __syncthreads();
-    for (int e = tid; e < kT * DKP; e += kThreads) {
-      const int t = e / DKP, i = e - t * DKP;
-      const int64_t tt = t0 + t;
-      const bool in = tt < L && i < dk;
-      const float qv = in ? Io<IoT>::to_f32(qg[tt * dk + i]) : 0.0f;
-      const float kv = in ? Io<IoT>::to_f32(kg[tt * dk + i]) : 0.0f;
-      sQ[t][i] = qv;
-      sK[t][i] = kv;
-      sKT[i][t] = kv;
-    }
-    {
-      const int t = tid / kCols, j = tid - t * kCols;  // kThreads == kT * kCols
-      const int64_t tt = t0 + t;
-      sVT[j][t] = (tt < L && j0 + j < dv) ? Io<IoT>::to_f32(vg[tt * dv + j0 + j]) : 0.0f;
-      if (tid < kT) sG[tid] = t0 + tid < L ? gg[t0 + tid] : 1.0f;
-    }
-    __syncthreads();
-    {
-      // L[t][s] = gamma_{s+1} ... gamma_t (s <= t), P[t] = gamma_0 L[t][0]
-      const int t = tid / kT, s = tid - t * kT;
-      float prod = 1.0f;
-      for (int i = s + 1; i <= t; ++i) prod *= sG[i];
-      sL[t][s] = s <= t ? prod : 0.0f;
-      if (s == 0) sP[t] = sG[0] * prod;
-    }
-    __syncthreads();
-
-    // 2. A^T[s][t] = sum over this wave's rows i of k[s][i] q[t][i]
-    v4f At = {0.0f, 0.0f, 0.0f, 0.0f};
+    // A^T[s][t] = k_s . q_t: register r at lane (t, G) is s = 4 G + r
+    v4f A0 = {0.0f, 0.0f, 0.0f, 0.0f}, A1 = A0;
     v4f qa[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int i = i0w + 16 * rt + 4 * G;
-      const v4f ka = *reinterpret_cast<const v4f*>(&sK[c16][i]);
-      qa[rt] = *reinterpret_cast<const v4f*>(&sQ[c16][i]);
+      const int i = 16 * rt + 4 * G;
+      const v4f ka = ld4(&s.k[c16][i]);
+      qa[rt] = ld4(&s.q[c16][i]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) At = mfma4(ka[g], qa[rt][g], At);
+      for (int g = 0; g < 4; ++g) {
+        if (rt & 1) A1 = mfma4(ka[g], qa[rt][g], A1);
+        else A0 = mfma4(ka[g], qa[rt][g], A0);
+      }
     }
-    // 3. M^T[s][t] = A^T[s][t] L[t][s]; register r holds s = 4G + r, t = c16
-    const v4f lt = *reinterpret_cast<const v4f*>(&sL[c16][4 * G]);
-    const v4f mt = At * lt;
-    // 4. Y[t][j] = sum_s M[t][s] v[s][j]  (contraction slot of step g: s = 4G + g)
-    const v4f vb = *reinterpret_cast<const v4f*>(&sVT[c16][4 * G]);
+    // M[t][s] = A[t][s] L[t][s]: the A operand of M V with slot s = 4 G + g
+    const v4f mt = (A0 + A1) * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
+    const v4f vb = ld4(&s.vg[G * St::VGS + (16 * w + c16) * 4]);  // v[4 G + g][column]
     v4f Y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < 4; ++g) Y = mfma4(mt[g], vb[g], Y);
-    // 5. Y[t][j] += P[t] sum over this wave's rows i of q[t][i] S_prev[i][j]
-    v4f Z = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Z[t][j] = q_t . S_prev[:, j]
+    v4f Z0 = {0.0f, 0.0f, 0.0f, 0.0f}, Z1 = Z0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (rt & 1) Z1 = mfma4(qa[rt][g], S[rt][g], Z1);
+        else Z0 = mfma4(qa[rt][g], S[rt][g], Z0);
+      }
+    Y += *reinterpret_cast<const v4f*>(&s.P[4 * G]) * (Z0 + Z1);
+    // S <- P_15 S + sum_s (L[15][s] k_s) v_s^T
+    const float p15 = s.P[kT - 1];
+    const v4f l15 = *reinterpret_cast<const v4f*>(&s.L[kT - 1][4 * G]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const v4f sa = *reinterpret_cast<const v4f*>(&sST[c16][i0w + 16 * rt + 4 * G]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) Z = mfma4(qa[rt][g], sa[g], Z);
-    }
-    const v4f pt = *reinterpret_cast<const v4f*>(&sP[4 * G]);
-    Y += pt * Z;
-    // 6. S <- P_15 S + sum_s (k[s][i] L[15][s]) v[s][j]
-    const float p15 = sP[kT - 1];
-    const v4f l15 = *reinterpret_cast<const v4f*>(&sL[kT - 1][4 * G]);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const v4f kt = *reinterpret_cast<const v4f*>(&sKT[i0w + 16 * rt + c16][4 * G]) * l15;
+      const v4f kt = ld4(&s.kg[G * St::KGS + (16 * rt + c16) * 4]) * l15;
       S[rt] *= p15;
 #pragma unroll
       for (int g = 0; g < 4; ++g) S[rt] = mfma4(kt[g], vb[g], S[rt]);
     }
-    publish_state();
-    // 7. this wave's partial y
-    *reinterpret_cast<v4f*>(&sYT[w][c16][4 * G]) = Y;
-    __syncthreads();
-
-    // 8. sum the partials and store y (16 threads per token: contiguous columns)
-    {
-      const int t = tid / kCols, j = tid - t * kCols;
-      const int64_t tt = t0 + t;
-      float acc = 0.0f;
+    // y: register r at lane (column, G) is token 4 G + r
+    if (jc < dv) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) acc += sYT[ww][j][t];
-      if (tt < L && j0 + j < dv) static_cast<IoT*>(p.y)[(b * L + tt) * dv + j0 + j] = Io<IoT>::from_f32(acc);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tt = t0 + 4 * G + r;
+        if (tt < L) static_cast<IoT*>(p.y)[(b * L + tt) * dv + jc] = Io<IoT>::from_f32(Y[r]);
+      }
     }
   }
 
-  if (p.final_state && jg < dv) {
+  if (p.final_state && jc < dv) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = i0w + 16 * rt + 4 * G + r;
-        if (i < dk) static_cast<StT*>(p.final_state)[(b * dk + i) * dv + jg] = Io<StT>::from_f32(S[rt][r]);
+        const int i = 16 * rt + 4 * G + r;
+        if (i < dk) static_cast<StT*>(p.final_state)[(b * dk + i) * dv + jc] = Io<StT>::from_f32(S[rt][r]);
       }
   }
 }
@@ -205,17 +305,24 @@ hipError_t launch_rt(const GatedParams& p0, hipStream_t stream) {
   p.col_blocks = (p.dv + kCols - 1) / kCols;
   const int64_t blocks = p.batch * p.col_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // 16-byte vectors: whole vectors per row and 16-byte aligned bases
+  constexpr int VEC_E = 16 / sizeof(IoT);
+  const bool vec = p.dk % VEC_E == 0 && p.dv % VEC_E == 0 && reinterpret_cast<uintptr_t>(p.q) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.k) % 16 == 0 && reinterpret_cast<uintptr_t>(p.v) % 16 == 0;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT>), dim3((unsigned)blocks),
-                         dim3(kThreads), args, 0, stream);
+  const void* fn = vec ? reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, true>)
+                       : reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
 }
 
 template <typename IoT, typename StT>
 hipError_t launch_io(const GatedParams& p, hipStream_t stream) {
-  if (p.dk <= 64) return launch_rt<IoT, StT, 1>(p, stream);
-  if (p.dk <= 128) return launch_rt<IoT, StT, 2>(p, stream);
-  if (p.dk <= 192) return launch_rt<IoT, StT, 3>(p, stream);
-  return launch_rt<IoT, StT, 4>(p, stream);
+  if (p.dk <= 16) return launch_rt<IoT, StT, 1>(p, stream);
+  if (p.dk <= 32) return launch_rt<IoT, StT, 2>(p, stream);
+  if (p.dk <= 64) return launch_rt<IoT, StT, 4>(p, stream);
+  if (p.dk <= 128) return launch_rt<IoT, StT, 8>(p, stream);
+  if (p.dk <= 192) return launch_rt<IoT, StT, 12>(p, stream);
+  return launch_rt<IoT, StT, 16>(p, stream);
 }
 
 }  // namespace
