@@ -30,8 +30,9 @@
 // 4-token groups [t / 4][row][t % 4] (the operands that contract over tokens
 // need 4 consecutive tokens of one row per lane), plus L and P. The next
 // chunk's q, k, v are loaded into registers with 16-byte loads, and its gamma
-// into scalar registers, while the current chunk is computed. Inputs whose
-// rows are not whole 16-byte vectors take a slower element-wise path.
+// one token per lane, while the current chunk is computed (no scalar loads in
+// the loop: they would share the LDS wait counter). Inputs whose rows are not
+// whole 16-byte vectors take a slower element-wise path.
 //
 // Rows of dk past dk, columns past dv and tokens past L are staged as zeros
 // (gamma as 1): they change nothing and are never stored.
@@ -83,14 +84,6 @@ __device__ __forceinline__ E elem(const u32x4 v, int e) {
   }
 }
 
-// A block-uniform pointer as a constant-address-space pointer, so that loads
-// through it at uniform indices are scalar loads.
-__device__ __forceinline__ const __attribute__((address_space(4))) float* uniform_f32(const float* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  return (const __attribute__((address_space(4))) float*)((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 template <typename E, int RT>
 struct Stage {
@@ -107,7 +100,8 @@ struct Stage {
 };
 
 template <typename IoT, typename StT, int RT, bool VEC>
-__global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 8 ? 3 : 1))) void gated_scan_kernel(
+    const GatedParams p) {
   using St = Stage<IoT, RT>;
   constexpr int DKP = St::DKP;
   constexpr int VEC_E = 16 / sizeof(IoT);            // elements per 16-byte vector
@@ -150,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams 
 
   // ---- the next chunk, in registers (q, k, v: vector path only)
   u32x4 qr[NQV], kr[NQV], vr;
-  float gam[kT];
+  float gam;
   auto prefetch = [&](int64_t t0) {
     if constexpr (VEC) {
 #pragma unroll
@@ -170,15 +164,8 @@ __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams 
         vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 + t) * dv + jb + j) : u32x4{0, 0, 0, 0};
       }
     }
-    // one load per token at a clamped index and a select (tokens past L
-    // read gamma 1): no branch, so every value reaches its use directly
-    const auto* gp = uniform_f32(gg);
-#pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      const bool in = t0 + u < L;
-      const float g = gp[in ? t0 + u : L - 1];
-      gam[u] = in ? g : 1.0f;
-    }
+    // gamma of token t0 + (tid mod 16), 1 past L
+    gam = t0 + (tid & 15) < L ? gg[t0 + (tid & 15)] : 1.0f;
   };
 
   auto write_stage = [&](St& s, int64_t t0) {
@@ -217,14 +204,20 @@ __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams 
         s.vg[(t >> 2) * St::VGS + j * 4 + (t & 3)] = in ? vgp[(t0 + t) * dv + jb + j] : zero_elem<IoT>();
       }
     }
-    // L[t][s] = gamma_{s+1} ... gamma_t (s <= t), P[t] = gamma_0 L[t][0]
+    // Thread 16 t + u holds gamma_u. Over each 16-lane row (one t), the
+    // suffix products of a_u = (u <= t ? gamma_u : 1) give
+    // L[t][s] = a_{s+1} ... a_15 = gamma_{s+1} ... gamma_t and
+    // P[t] = a_0 ... a_15 = gamma_0 ... gamma_t.
     {
-      const int t = tid >> 4, sidx = tid & 15;
-      float prod = 1.0f;
-#pragma unroll
-      for (int u = 1; u < kT; ++u) prod *= (u > sidx && u <= t) ? gam[u] : 1.0f;
-      s.L[t][sidx] = sidx <= t ? prod : 0.0f;
-      if (sidx == 0) s.P[t] = gam[0] * prod;
+      const int t = tid >> 4, u = tid & 15;
+      float x = u <= t ? gam : 1.0f;
+      x *= dpp_or<kDppRowShl1>(1.0f, x);
+      x *= dpp_or<kDppRowShl1 + 1>(1.0f, x);
+      x *= dpp_or<kDppRowShl1 + 3>(1.0f, x);
+      x *= dpp_or<kDppRowShl1 + 7>(1.0f, x);
+      const float after = dpp_or<kDppRowShl1>(1.0f, x);  // a_{u+1} ... a_15
+      s.L[t][u] = u <= t ? after : 0.0f;
+      if (u == 0) s.P[t] = x;
     }
   };
 
@@ -240,16 +233,15 @@ __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams 
 
     // A^T[s][t] = k_s . q_t: register r at lane (t, G) is s = 4 G + r
     v4f A0 = {0.0f, 0.0f, 0.0f, 0.0f}, A1 = A0;
-    v4f qa[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int i = 16 * rt + 4 * G;
       const v4f ka = ld4(&s.k[c16][i]);
-      qa[rt] = ld4(&s.q[c16][i]);
+      const v4f qa = ld4(&s.q[c16][i]);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (rt & 1) A1 = mfma4(ka[g], qa[rt][g], A1);
-        else A0 = mfma4(ka[g], qa[rt][g], A0);
+        if (rt & 1) A1 = mfma4(ka[g], qa[g], A1);
+        else A0 = mfma4(ka[g], qa[g], A0);
       }
     }
     // M[t][s] = A[t][s] L[t][s]: the A operand of M V with slot s = 4 G + g
@@ -259,14 +251,17 @@ __global__ __launch_bounds__(kThreads) void gated_scan_kernel(const GatedParams 
 #pragma unroll
     for (int g = 0; g < 4; ++g) Y = mfma4(mt[g], vb[g], Y);
     // Z[t][j] = q_t . S_prev[:, j]
+    asm volatile("" ::: "memory");  // q is read again below rather than held
     v4f Z0 = {0.0f, 0.0f, 0.0f, 0.0f}, Z1 = Z0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const v4f qa = ld4(&s.q[c16][16 * rt + 4 * G]);  // read again: fewer live registers
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if (rt & 1) Z1 = mfma4(qa[rt][g], S[rt][g], Z1);
-        else Z0 = mfma4(qa[rt][g], S[rt][g], Z0);
+        if (rt & 1) Z1 = mfma4(qa[g], S[rt][g], Z1);
+        else Z0 = mfma4(qa[g], S[rt][g], Z0);
       }
+    }
     Y += *reinterpret_cast<const v4f*>(&s.P[4 * G]) * (Z0 + Z1);
     // S <- P_15 S + sum_s (L[15][s] k_s) v_s^T
     const float p15 = s.P[kT - 1];
