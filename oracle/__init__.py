@@ -11,7 +11,11 @@ channel) rows over threads (ctypes releases the GIL during each call). Rows
 never interact, so the split changes no result: every row's token loop stays
 sequential in one call.
 
-Every function here is pinned by ``tests/test_oracle_pins.py``.
+Every function here is pinned: the scan and the decode step by
+``tests/test_oracle_pins.py``, the scalar-gated scan by
+``tests/test_oracle_gated_pins.py``, the effective attention by
+``tests/test_oracle_attention_pins.py``; ``tests/test_oracle_mutants.py``
+checks that the pins catch planted mistakes.
 """
 from __future__ import annotations
 
@@ -53,6 +57,9 @@ def _load():
         lib.oracle_update.argtypes = [i64, i64, i64] + [dp] * 9 + [ctypes.c_int, dp, i64, i64]
         lib.oracle_gated_scan.restype = ctypes.c_int
         lib.oracle_gated_scan.argtypes = [i64, i64, i64, i64] + [dp] * 7 + [i64, i64]
+        lib.oracle_effective_attention.restype = ctypes.c_int
+        lib.oracle_effective_attention.argtypes = [i64, i64, i64, i64] + [dp] * 5 + [ctypes.c_int] * 3 + [
+            dp, i64, i64]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         _lib = lib
@@ -209,3 +216,45 @@ def gated_scan(q, k, v, gamma, s0=None, threads=None):
         with ThreadPoolExecutor(len(parts)) as ex:
             list(ex.map(run, parts))
     return y, fs
+
+
+def effective_attention(dt, A, B, C, dt_bias=None, dt_softplus=True, include_dt_scaling=False,
+                        per_state_coord=False, threads=None):
+    """Effective attention of the selective scan (TransformerLens "ssm_mixer"
+    page, compute_effective_attention):
+    M[b, c, i, j] = sum_n C[b, n, i] prod_{k=j+1..i} exp(A[c, n] dt[b, c, k]) B[b, n, j]
+    for j <= i, 0 above the diagonal; dt is the step size of the scan
+    (softplus(dt + dt_bias) or dt + dt_bias). include_dt_scaling multiplies
+    column j by dt[b, c, j] (then y = M x + D x before the gate);
+    per_state_coord returns the terms unsummed over n.
+    dt: [batch, channels, L]; A: [channels, N]; B, C: [batch, N, L].
+    Returns [batch, channels, L, L] or [batch, channels, N, L, L] in fp64."""
+    lib = _load()
+    dt = _f64(dt)
+    batch, channels, L = dt.shape
+    A = _f64(A)
+    if A.ndim != 2 or A.shape[0] != channels:
+        raise ValueError(f"A must be [channels, N], got {A.shape}")
+    N = A.shape[1]
+    B = _f64(B, (batch, N, L))
+    C = _f64(C, (batch, N, L))
+    dt_bias = _f64(dt_bias, (channels,))
+    shape = (batch, channels, N, L, L) if per_state_coord else (batch, channels, L, L)
+    out = np.empty(shape, dtype=np.float64)
+    if batch * channels == 0:
+        return out
+
+    def run(rng):
+        rc = lib.oracle_effective_attention(batch, channels, N, L, _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                            _ptr(dt_bias), int(bool(dt_softplus)), int(bool(include_dt_scaling)),
+                                            int(bool(per_state_coord)), _ptr(out), rng[0], rng[1])
+        if rc != 0:
+            raise ValueError(f"oracle_effective_attention rejected its arguments (code {rc})")
+
+    parts = _split_rows(batch * channels, _threads(threads))
+    if len(parts) == 1:
+        run(parts[0])
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+    return out

@@ -182,3 +182,57 @@ int oracle_gated_scan(int64_t batch, int64_t L, int64_t dk, int64_t dv,
     free(S);
     return ORACLE_OK;
 }
+
+/*
+ * Effective attention of the selective scan (TransformerLens "ssm_mixer"
+ * page, compute_effective_attention): per batch item and channel,
+ *
+ *   M[c, i, j] = sum_n C[i, n] * prod_{k=j+1..i} exp(A[c, n] * dt[c, k]) * B[j, n]
+ *
+ * for j <= i (the product is empty, 1, at j == i) and 0 for j > i (causal).
+ * dt is the step size (softplus of dt_raw + dt_bias, or dt_raw + dt_bias, as
+ * in the scan). With include_dt nonzero column j is multiplied by dt[c, j]
+ * (the page's reconstruction form, y = M x + D x before the gate). With
+ * per_state nonzero the sum over n is not taken.
+ *   dt          : [batch, channels, L]
+ *   Bm, Cm      : [batch, N, L];  A : [channels, N];  dt_bias : [channels]
+ *   out         : [batch, channels, L, L], or [batch, channels, N, L, L]
+ * The product for column j is accumulated over i = j+1, j+2, ... one factor
+ * at a time, in the order the page writes it. Rows r = b * channels + c in
+ * [row_begin, row_end).
+ */
+int oracle_effective_attention(int64_t batch, int64_t channels, int64_t N, int64_t L,
+                               const double* dt, const double* A, const double* Bm, const double* Cm,
+                               const double* dt_bias, int dt_softplus, int include_dt, int per_state,
+                               double* out, int64_t row_begin, int64_t row_end) {
+    if (batch < 0 || channels < 0 || N < 1 || N > 4096 || L < 0) return ORACLE_BAD_ARG;
+    if (!dt || !A || !Bm || !Cm || !out) return ORACLE_BAD_ARG;
+    if (row_begin < 0 || row_end > batch * channels || row_begin > row_end) return ORACLE_BAD_ARG;
+    double* d = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double prod[4096];
+    if (!d) return ORACLE_BAD_ARG;
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const int64_t b = r / channels, c = r % channels;
+        const double* Bb = Bm + b * N * L;
+        const double* Cb = Cm + b * N * L;
+        for (int64_t t = 0; t < L; ++t) d[t] = step_size(dt[r * L + t], dt_bias, c, dt_softplus);
+        double* o = out + r * (per_state ? N : 1) * L * L;
+        for (int64_t j = 0; j < L; ++j) {
+            for (int64_t n = 0; n < N; ++n) prod[n] = 1.0;
+            const double colscale = include_dt ? d[j] : 1.0;
+            for (int64_t i = 0; i < L; ++i) {
+                if (i > j)
+                    for (int64_t n = 0; n < N; ++n) prod[n] *= exp(A[c * N + n] * d[i]);
+                double m = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double term = i >= j ? Cb[n * L + i] * prod[n] * Bb[n * L + j] * colscale : 0.0;
+                    if (per_state) o[(n * L + i) * L + j] = term;
+                    m += term;
+                }
+                if (!per_state) o[i * L + j] = m;
+            }
+        }
+    }
+    free(d);
+    return ORACLE_OK;
+}

@@ -10,6 +10,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_attention_pins as apins
 from tests import test_oracle_gated_pins as gpins
 from tests import test_oracle_pins as pins
 
@@ -54,6 +55,13 @@ MUTANTS = {
     "gated_initial_state_ignored": ("S[e] = s0 ? s0[b * dk * dv + e] : 0.0;", "S[e] = 0.0;"),
     "gated_gate_of_next_token": ("const double g = gamma[b * L + t];",
                                  "const double g = gamma[b * L + (t + 1 < L ? t + 1 : t)];"),
+    # effective attention
+    "attn_product_includes_j": ("if (i > j)\n                    for (int64_t n = 0; n < N; ++n) prod[n] *=",
+                                "if (i >= j)\n                    for (int64_t n = 0; n < N; ++n) prod[n] *="),
+    "attn_decay_of_column_token": ("prod[n] *= exp(A[c * N + n] * d[i]);", "prod[n] *= exp(A[c * N + n] * d[j]);"),
+    "attn_B_C_swapped": ("Cb[n * L + i] * prod[n] * Bb[n * L + j]", "Bb[n * L + i] * prod[n] * Cb[n * L + j]"),
+    "attn_not_causal": ("i >= j ? Cb[n * L + i]", "1 ? Cb[n * L + i]"),
+    "attn_row_scaled": ("Bb[n * L + j] * colscale", "Bb[n * L + j] * (include_dt ? d[i] : 1.0)"),
 }
 
 
@@ -79,6 +87,14 @@ def _pin_callables():
             calls.append((name, lambda fn=fn: fn(2, True)))
         else:
             calls.append((name, fn))
+    for name in dir(apins):
+        if not name.startswith("test_apin"):
+            continue
+        fn = getattr(apins, name)
+        if name == "test_apin1_reconstructs_the_scan":
+            calls.append((name, lambda fn=fn: fn(True)))
+        else:
+            calls.append((name, fn))
     return calls
 
 
@@ -101,7 +117,8 @@ def test_pins_catch_mutant(mutant, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(old, new, tmp)
         lib = ctypes.CDLL(so)
-        for fn in ("oracle_scan", "oracle_update", "oracle_softplus", "oracle_gated_scan"):
+        for fn in ("oracle_scan", "oracle_update", "oracle_softplus", "oracle_gated_scan",
+                   "oracle_effective_attention"):
             getattr(lib, fn).restype = getattr(real, fn).restype
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         monkeypatch.setattr(oracle, "_lib", lib)
