@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 4
+#define SS_ABI_VERSION 5
 #define SS_MAX_STATE_DIM 64
 #define SS_MAX_GATED_DK 256
 
@@ -170,6 +170,41 @@ int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_d
 int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_dtype, int state_dtype,
                   const void* q, const void* k, const void* v, const float* gamma, const void* s0, void* y,
                   void* final_state, void* stream);
+
+/*
+ * Effective attention of the selective scan (TransformerLens "ssm_mixer"
+ * page, compute_effective_attention): per batch item b and channel c,
+ *
+ *   M[b, c, i, j] = sum_n C[b, n, i] * prod_{k=j+1..i} exp(A[c, n] * dt[b, c, k]) * B[b, n, j]
+ *
+ * for j <= i (the empty product at j == i is 1) and 0 for j > i, in fp32.
+ * dt is the scan's step size: softplus(dt + dt_bias) when dt_softplus is
+ * nonzero, else dt + dt_bias (dt_bias NULL = 0), as in ss_scan_fwd.
+ * include_dt_scaling nonzero multiplies column j by dt[b, c, j], the page's
+ * reconstruction form (sum_j M[b, c, i, j] x[b, c, j] + D[c] x[b, c, i] is
+ * ss_scan_fwd's output before the gate, from a zero state, without resets).
+ * per_state_coord nonzero keeps the terms per state coordinate n instead of
+ * summing them.
+ *
+ *   dt          : [batch, channels, seqlen]       io_dtype
+ *   A           : [channels, state_dim]           float32
+ *   B, C        : [batch, state_dim, seqlen]      io_dtype
+ *   dt_bias     : [channels] float32, or NULL
+ *   M           : output float32, [batch, channels, seqlen, seqlen], or
+ *                 [batch, channels, state_dim, seqlen, seqlen] with
+ *                 per_state_coord; every element is written (zeros above
+ *                 the diagonal)
+ *
+ * The output grows as seqlen^2 (the page meant it for short sequences); its
+ * size must fit in int64 bytes (else SS_ERR_SHAPE). state_dim must be in
+ * [1, SS_MAX_STATE_DIM]. batch, channels or seqlen == 0 is a no-op returning
+ * SS_OK. M must not overlap any input (SS_ERR_ALIAS). Conventions of the
+ * other calls hold (device pointers, asynchronous on `stream`, validation
+ * before any launch, inputs untouched, bitwise reproducible).
+ */
+int ss_effective_attention(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
+                           const void* dt, const float* A, const void* B, const void* C, const float* dt_bias,
+                           int dt_softplus, int include_dt_scaling, int per_state_coord, float* M, void* stream);
 
 /* Static, NUL-terminated name of a status code (unknown codes included). */
 const char* ss_status_str(int status);

@@ -19,6 +19,11 @@ and the scalar-gated state scan of the "Mamba 2 Gated State Scan" page:
 
     ss_gated_scan(q, k, v, gamma, s0=None) -> (y, final_state)
 
+and the scan's effective attention of the TransformerLens "ssm_mixer" page:
+
+    ss_effective_attention(dt, A, B, C, dt_bias=None, include_dt_scaling=False,
+                           per_state_coord=False) -> M
+
 Arguments are torch tensors on the GPU: the binding checks them, allocates
 the outputs with torch and passes raw device pointers plus the current HIP
 stream. Every step of the computation runs in the library's kernels; there is
@@ -29,6 +34,7 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     SSError,
     abi_version,
+    ss_effective_attention,
     ss_gated_scan,
     library_path,
     load_library,

@@ -46,6 +46,8 @@ def load_library() -> ctypes.CDLL:
     lib.ss_scan_fwd_states.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp, i64, vp]
     lib.ss_gated_scan.restype = i32
     lib.ss_gated_scan.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 7 + [vp]
+    lib.ss_effective_attention.restype = i32
+    lib.ss_effective_attention.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.ss_state_update.restype = i32
     lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
     lib.ss_status_str.restype = ctypes.c_char_p
@@ -239,6 +241,50 @@ def ss_gated_scan(q, k, v, gamma, s0=None, *, state_dtype=None, y=None, final_st
     if rc != SS_OK:
         raise SSError(rc, "ss_gated_scan")
     return y, final_state
+
+
+def ss_effective_attention(dt, A, B, C, dt_bias=None, *, dt_softplus: bool = True,
+                           include_dt_scaling: bool = False, per_state_coord: bool = False, out=None,
+                           stream=None):
+    """Effective attention of the selective scan on the GPU:
+    M[b, c, i, j] = sum_n C[b, n, i] prod_{k=j+1..i} exp(A[c, n] dt[b, c, k]) B[b, n, j]
+    for j <= i, 0 above the diagonal, with dt the scan's step size
+    (softplus(dt + dt_bias) unless dt_softplus is False). dt: [batch,
+    channels, seq]; B, C: [batch, state_dim, seq] (float32 or bfloat16, one
+    dtype); A: [channels, state_dim] float32; dt_bias: [channels] float32 or
+    None. include_dt_scaling multiplies column j by dt_j (then y = M x + D x
+    before the gate); per_state_coord keeps the state coordinate axis.
+    Returns float32 [batch, channels, seq, seq] or [batch, channels,
+    state_dim, seq, seq] (written into `out` when given)."""
+    import torch
+    if dt.dim() != 3 or A.dim() != 2:
+        raise ValueError("dt must be [batch, channels, seq] and A [channels, state_dim]")
+    batch, channels, L = dt.shape
+    N = A.shape[1]
+    dev = dt.device
+    if dev.type != "cuda":
+        raise ValueError("ss_effective_attention runs on the GPU: dt must be a device tensor")
+    io = dt.dtype
+    code = _io_code(io)
+    dt, A, B, C = dt.contiguous(), A.contiguous(), B.contiguous(), C.contiguous()
+    _check(A, "A", (channels, N), torch.float32, dev)
+    _check(B, "B", (batch, N, L), io, dev)
+    _check(C, "C", (batch, N, L), io, dev)
+    if dt_bias is not None:
+        dt_bias = dt_bias.contiguous()
+        _check(dt_bias, "dt_bias", (channels,), torch.float32, dev)
+    shape = (batch, channels, N, L, L) if per_state_coord else (batch, channels, L, L)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    else:
+        _check(out, "out", shape, torch.float32, dev)
+    rc = load_library().ss_effective_attention(batch, channels, N, L, code, _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                               _ptr(dt_bias), int(bool(dt_softplus)),
+                                               int(bool(include_dt_scaling)), int(bool(per_state_coord)),
+                                               _ptr(out), _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_effective_attention")
+    return out
 
 
 def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True, *, y=None,

@@ -134,6 +134,33 @@ int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
+int ss_effective_attention(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
+                           const void* dt, const float* A, const void* B, const void* C, const float* dt_bias,
+                           int dt_softplus, int include_dt_scaling, int per_state_coord, float* M, void* stream) {
+  const ss::AttnArgs a{batch, channels, state_dim, seqlen, io_dtype, dt, A, B, C, dt_bias,
+                       dt_softplus, include_dt_scaling, per_state_coord, M};
+  bool noop = false;
+  const ss_status st = ss::validate_attention(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (ss::effective_attention_blocks(batch, channels, seqlen) > 0x7fffffff) return SS_ERR_SHAPE;
+  ss::AttnParams p{};
+  p.batch = batch;
+  p.channels = channels;
+  p.L = seqlen;
+  p.N = (int)state_dim;
+  p.dt = dt;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.dt_bias = dt_bias;
+  p.dt_softplus = dt_softplus != 0;
+  p.include_dt = include_dt_scaling != 0;
+  p.per_state = per_state_coord != 0;
+  p.M = M;
+  const hipError_t e = ss::launch_effective_attention(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
 const char* ss_status_str(int status) {
   switch (status) {
     case SS_OK: return "SS_OK";

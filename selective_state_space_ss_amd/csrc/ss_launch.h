@@ -75,6 +75,22 @@ hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t str
 bool scan_rows_supported(const ScanParams& p, bool io_bf16);
 hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
 // The scalar-gated state scan (gated_scan.hip); io_bf16: element type of q, k, v, y.
+// Effective attention; see ss_effective_attention in ss_scan.h.
+struct AttnParams {
+  int64_t batch, channels, L;
+  int N;
+  int64_t jblocks;      // ceil(L / columns per block)
+  const void* dt;       // [batch, channels, L]
+  const float* A;       // [channels, N]
+  const void* B;        // [batch, N, L]
+  const void* C;        // [batch, N, L]
+  const float* dt_bias; // [channels] or nullptr
+  int dt_softplus, include_dt, per_state;
+  float* M;             // [batch, channels, L, L] or [batch, channels, N, L, L]
+};
+
+hipError_t launch_effective_attention(const AttnParams& p, bool io_bf16, hipStream_t stream);
+
 // io_bf16: element type of q, k, v, y; state_bf16: that of s0 and final_state.
 hipError_t launch_gated_scan(const GatedParams& p, bool io_bf16, bool state_bf16, hipStream_t stream);
 
@@ -85,4 +101,5 @@ namespace ss {
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
 bool state_update_grid_ok(int64_t batch, int64_t channels, int64_t state_dim);
 int64_t gated_scan_blocks(int64_t batch, int64_t dv);
+int64_t effective_attention_blocks(int64_t batch, int64_t channels, int64_t L);
 }  // namespace ss

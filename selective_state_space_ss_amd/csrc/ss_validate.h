@@ -165,6 +165,51 @@ inline ss_status validate_gated(const GatedArgs& a, bool* noop) {
   return SS_OK;
 }
 
+// Inputs of the effective attention, in ABI order; see ss_effective_attention.
+struct AttnArgs {
+  int64_t batch, channels, state_dim, seqlen;
+  int io_dtype;
+  const void* dt;
+  const float* A;
+  const void *B, *C;
+  const float* dt_bias;
+  int dt_softplus, include_dt_scaling, per_state_coord;
+  float* M;
+};
+
+inline ss_status validate_attention(const AttnArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.channels < 0 || a.state_dim < 0 || a.seqlen < 0) return SS_ERR_SHAPE;
+  if (a.state_dim < 1 || a.state_dim > SS_MAX_STATE_DIM) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0 || a.channels == 0 || a.seqlen == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t bc, bcl, x_bytes, bn, bnl, bc_bytes, a_elems, a_bytes, ll, m, m_bytes;
+  if (!mul_ok(a.batch, a.channels, &bc) || !mul_ok(bc, a.seqlen, &bcl) || !mul_ok(bcl, es, &x_bytes) ||
+      !mul_ok(a.batch, a.state_dim, &bn) || !mul_ok(bn, a.seqlen, &bnl) || !mul_ok(bnl, es, &bc_bytes) ||
+      !mul_ok(a.channels, a.state_dim, &a_elems) || !mul_ok(a_elems, 4, &a_bytes) ||
+      !mul_ok(a.seqlen, a.seqlen, &ll) || !mul_ok(bc, ll, &m) ||
+      !mul_ok(m, a.per_state_coord ? a.state_dim : 1, &m) || !mul_ok(m, 4, &m_bytes))
+    return SS_ERR_SHAPE;
+  if (x_bytes > (INT64_MAX >> 2) || m_bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  if (!a.dt || !a.A || !a.B || !a.C || !a.M) return SS_ERR_NULL;
+  const void* io_ptrs[] = {a.dt, a.B, a.C};
+  for (const void* p : io_ptrs)
+    if (!aligned(p, es)) return SS_ERR_ALIGN;
+  const void* f32_ptrs[] = {a.A, a.dt_bias, a.M};
+  for (const void* p : f32_ptrs)
+    if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+  const Span out(a.M, m_bytes);
+  const Span inputs[] = {Span(a.dt, x_bytes), Span(a.A, a_bytes), Span(a.B, bc_bytes), Span(a.C, bc_bytes),
+                         Span(a.dt_bias, a.channels * 4)};
+  for (const Span& in : inputs)
+    if (out.overlaps(in)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
 // Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
 struct UpdateArgs {
   int64_t batch, channels, state_dim;

@@ -31,8 +31,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ss_abi_version", "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_states",
-                                    "ss_state_update", "ss_status_str"]
+    assert declared_functions() == ["ss_abi_version", "ss_effective_attention", "ss_gated_scan", "ss_scan_fwd",
+                                    "ss_scan_fwd_states", "ss_state_update", "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 4
+    assert ss.abi_version() == 5
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -132,6 +132,27 @@ def test_gated_validation(lib):
     assert gated_call(lib, s0=6 * MB, final_state=6 * MB + 4) == ALIAS     # partial overlap with s0
     assert gated_call(lib, batch=1 << 40, L=1 << 40) == SHAPE
     assert gated_call(lib, batch=0) == OK
+
+
+def attn_call(lib, batch=2, channels=3, N=16, L=64, io=1, dt=1 * MB, A=2 * MB, B=3 * MB, C=4 * MB,
+              dt_bias=None, per_state=0, M=6 * MB):
+    return lib.ss_effective_attention(batch, channels, N, L, io, dt, A, B, C, dt_bias, 1, 0, per_state, M, None)
+
+
+def test_attention_validation(lib):
+    assert attn_call(lib, io=7) == DTYPE
+    assert attn_call(lib, L=-1) == SHAPE
+    assert attn_call(lib, N=0) == UNSUP
+    assert attn_call(lib, N=65) == UNSUP
+    assert attn_call(lib, dt=None) == NULL
+    assert attn_call(lib, M=None) == NULL
+    assert attn_call(lib, B=3 * MB + 1) == ALIGN
+    assert attn_call(lib, M=6 * MB + 2) == ALIGN
+    assert attn_call(lib, M=1 * MB) == ALIAS                     # M over dt
+    assert attn_call(lib, M=4 * MB - 16) == ALIAS                # M runs into C
+    assert attn_call(lib, L=1 << 31, channels=1 << 20) == SHAPE  # M's bytes overflow
+    assert attn_call(lib, batch=0) == OK
+    assert attn_call(lib, L=0) == OK
 
 
 def test_update_validation(lib):
