@@ -64,7 +64,7 @@ def parse():
                     help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the per-token-states and gated-scan measurements")
+                    help="skip the per-token-states, gated-scan and effective-attention measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
@@ -208,6 +208,38 @@ def measure_gated(ss, stream, reps: int = 20):
             "us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "mfma_flops": flops,
             "TFLOP_s": round(tf, 2), "mfma_fp32_frac": round(tf / PEAK_FP32_TFLOPS, 4)}
+
+
+ATTN_SHAPE = (1, 1536, 16, 256)   # batch, channels, state_dim, seq
+
+
+def measure_attention(ss, stream, reps: int = 20):
+    """ss_effective_attention at batch 1, channels 1536, state_dim 16, seq 256,
+    bf16 inputs (a Mamba-130M-shaped layer on a short sequence), summed over
+    the state coordinate, fp32 output. Algorithmic bytes: the output (4 L^2
+    per channel) plus dt, B and C once; the row loop's work is 2 N VALU
+    operations per lower-triangle element."""
+    import torch
+    from selective_state_space_ss_amd.workloads import make_case
+    batch, channels, N, L = ATTN_SHAPE
+    inp = {k: (None if v is None else v.cuda())
+           for k, v in make_case(1020, batch, channels, N, L, "bf16", gate=False, h0=False).items()}
+    out = torch.empty(batch, channels, L, L, dtype=torch.float32, device="cuda")
+    f = lambda: ss.ss_effective_attention(inp["dt"], inp["A"], inp["B"], inp["C"], inp["dt_bias"], out=out)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = batch * channels * L * L * 4 + batch * channels * L * 2 + 2 * batch * N * L * 2 + channels * (N + 1) * 4
+    return {"shape": {"batch": batch, "channels": channels, "state_dim": N, "seq": L, "io": "bf16", "out": "f32"},
+            "us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline(inp, w, budget_s: float):
@@ -370,7 +402,8 @@ def main():
     }
     if not args.no_extras:
         out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream),
-                         "ss_gated_scan": measure_gated(ss, stream)}
+                         "ss_gated_scan": measure_gated(ss, stream),
+                         "ss_effective_attention": measure_attention(ss, stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -17,7 +17,8 @@
 // times that unsummed) is the dominant traffic; each row step of a wave
 // stores 64 consecutive columns (256 contiguous bytes).
 //
-// Layout. A block is (b, c) and 256 columns, one wave per 64 columns. Rows
+// Layout. A block is (b, c) and 256 columns, one wave per 64 columns (which
+// wave takes which 64 rotates with the block index, to balance the SIMDs). Rows
 // are walked in tiles of 64 tokens: the block stages exp(A[c, n] dt_i) and
 // C[b, n, i] for the tile in LDS ([token][n], so a lane reads four
 // coordinates per 16-byte broadcast read), then each wave walks the tile's
@@ -48,8 +49,12 @@ __global__ __launch_bounds__(kThreads) void effective_attention_kernel(const Att
   const int64_t jb = (blockIdx.x - bc * p.jblocks) * kCols;  // block's first column
   const int64_t b = bc / p.channels;
   const int64_t c = bc - b * p.channels;
-  const int64_t j = jb + tid;          // this lane's column
-  const int64_t jw = jb + 64 * w;      // this wave's first column
+  // Wave w of a block runs on SIMD w, and the triangle gives the first column
+  // group four times the rows of the last; rotating the group a wave takes
+  // by the block index spreads heavy and light groups over the SIMDs.
+  const int grp = (w + static_cast<int>(blockIdx.x & 3)) & 3;
+  const int64_t jw = jb + 64 * grp;    // this wave's first column
+  const int64_t j = jw + (tid & 63);   // this lane's column
   const bool live = j < L;
   const IoT* __restrict__ dtg = static_cast<const IoT*>(p.dt) + bc * L;
   const IoT* __restrict__ Bg = static_cast<const IoT*>(p.B) + b * N * L;
@@ -117,47 +122,44 @@ __global__ __launch_bounds__(kThreads) void effective_attention_kernel(const Att
     }
     __syncthreads();
     const int rows = static_cast<int>(L - i0 < kTile ? L - i0 : kTile);
+    // One row step: extend the products by row ii's factors (where the row
+    // is past the column, when masked) and contract with C. Reads are
+    // unconditional 16-byte broadcasts and the masks are selects, so the
+    // step has no branches; the contraction runs as two partial sums.
+    auto row_step = [&](int ii, bool masked, bool extend, bool on) {
+      float m0 = 0.0f, m1 = 0.0f;
+      float term[PER_STATE ? NMAX : 1];
+#pragma unroll
+      for (int n = 0; n < NMAX; n += 4) {
+        float4 a4 = *reinterpret_cast<const float4*>(&sa[ii][n]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sc[ii][n]);
+        if (masked) {
+          a4.x = extend ? a4.x : 1.0f; a4.y = extend ? a4.y : 1.0f;
+          a4.z = extend ? a4.z : 1.0f; a4.w = extend ? a4.w : 1.0f;
+        }
+        d[n] *= a4.x; d[n + 1] *= a4.y; d[n + 2] *= a4.z; d[n + 3] *= a4.w;
+        if constexpr (PER_STATE) {
+          term[n] = c4.x * d[n]; term[n + 1] = c4.y * d[n + 1];
+          term[n + 2] = c4.z * d[n + 2]; term[n + 3] = c4.w * d[n + 3];
+          if (masked && !on) term[n] = term[n + 1] = term[n + 2] = term[n + 3] = 0.0f;
+        } else {
+          m0 = __builtin_fmaf(c4.x, d[n], m0);
+          m1 = __builtin_fmaf(c4.y, d[n + 1], m1);
+          m0 = __builtin_fmaf(c4.z, d[n + 2], m0);
+          m1 = __builtin_fmaf(c4.w, d[n + 3], m1);
+        }
+      }
+      const float m = (masked && !on) ? 0.0f : m0 + m1;
+      if (live) store(i0 + ii, term, m);
+    };
     if (i0 + kTile <= jw) {  // above the diagonal for every column of this wave
       if (live)
         for (int ii = 0; ii < rows; ++ii) store_zero(i0 + ii);
     } else if (i0 >= jw + 64) {  // below it for every column of this wave
-      for (int ii = 0; ii < rows; ++ii) {
-        float m = 0.0f;
-#pragma unroll
-        for (int n = 0; n < NMAX; n += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(&sa[ii][n]);
-          const float4 c4 = *reinterpret_cast<const float4*>(&sc[ii][n]);
-          d[n] *= a4.x; d[n + 1] *= a4.y; d[n + 2] *= a4.z; d[n + 3] *= a4.w;
-          m = __builtin_fmaf(c4.x, d[n], m);
-          m = __builtin_fmaf(c4.y, d[n + 1], m);
-          m = __builtin_fmaf(c4.z, d[n + 2], m);
-          m = __builtin_fmaf(c4.w, d[n + 3], m);
-        }
-        if (live) {
-          if constexpr (PER_STATE) {
-            float term[NMAX];
-#pragma unroll
-            for (int n = 0; n < NMAX; ++n) term[n] = sc[ii][n] * d[n];
-            store(i0 + ii, term, m);
-          } else {
-            store(i0 + ii, nullptr, m);
-          }
-        }
-      }
+#pragma unroll 2
+      for (int ii = 0; ii < rows; ++ii) row_step(ii, false, true, true);
     } else {  // the wave's diagonal tile: rows i0 .. i0 + 63 against columns jw .. jw + 63
-      for (int ii = 0; ii < rows; ++ii) {
-        const int64_t i = i0 + ii;
-        const bool extend = i > j, on = i >= j;
-        float m = 0.0f;
-        float term[NMAX];
-#pragma unroll
-        for (int n = 0; n < NMAX; ++n) {
-          d[n] = extend ? d[n] * sa[ii][n] : d[n];
-          term[n] = on ? sc[ii][n] * d[n] : 0.0f;
-          m += term[n];
-        }
-        if (live) store(i, term, m);
-      }
+      for (int ii = 0; ii < rows; ++ii) row_step(ii, true, i0 + ii > j, i0 + ii >= j);
     }
   }
 }
