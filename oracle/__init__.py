@@ -14,7 +14,8 @@ sequential in one call.
 Every function here is pinned: the scan and the decode step by
 ``tests/test_oracle_pins.py``, the scalar-gated scan by
 ``tests/test_oracle_gated_pins.py``, the effective attention by
-``tests/test_oracle_attention_pins.py``; ``tests/test_oracle_mutants.py``
+``tests/test_oracle_attention_pins.py``, the conv1d + SiLU and dt_proj
+producers by ``tests/test_oracle_producer_pins.py``; ``tests/test_oracle_mutants.py``
 checks that the pins catch planted mistakes.
 """
 from __future__ import annotations
@@ -60,6 +61,10 @@ def _load():
         lib.oracle_effective_attention.restype = ctypes.c_int
         lib.oracle_effective_attention.argtypes = [i64, i64, i64, i64] + [dp] * 5 + [ctypes.c_int] * 3 + [
             dp, i64, i64]
+        lib.oracle_conv1d_silu.restype = ctypes.c_int
+        lib.oracle_conv1d_silu.argtypes = [i64, i64, i64, i64] + [dp] * 5 + [i64, i64]
+        lib.oracle_dt_proj.restype = ctypes.c_int
+        lib.oracle_dt_proj.argtypes = [i64, i64, i64, i64] + [dp] * 3 + [ctypes.c_int, dp, i64, i64]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         _lib = lib
@@ -258,3 +263,67 @@ def effective_attention(dt, A, B, C, dt_bias=None, dt_softplus=True, include_dt_
         with ThreadPoolExecutor(len(parts)) as ex:
             list(ex.map(run, parts))
     return out
+
+
+def _rows_parallel(rows, threads, run):
+    parts = _split_rows(rows, _threads(threads))
+    if len(parts) == 1:
+        run(parts[0])
+    elif parts:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, parts))
+
+
+def conv1d_silu(x_pre, conv_w, conv_b=None, reset=None, threads=None):
+    """Causal depthwise conv1d of width W = conv_w.shape[1], then SiLU:
+    x[b, c, t] = silu(conv_b[c] + sum_k conv_w[c, k] x_pre[b, c, t - (W-1) + k]),
+    taps before position 0 or before the current document's first token
+    (reset[b, s] != 0) reading 0. x_pre: [batch, channels, L]; conv_w:
+    [channels, W]; conv_b: [channels] or None; reset: [batch, L] or None.
+    Returns x [batch, channels, L] in fp64."""
+    lib = _load()
+    x_pre = _f64(x_pre)
+    batch, channels, L = x_pre.shape
+    conv_w = _f64(conv_w)
+    if conv_w.ndim != 2 or conv_w.shape[0] != channels:
+        raise ValueError(f"conv_w must be [channels, W], got {conv_w.shape}")
+    W = conv_w.shape[1]
+    conv_b = _f64(conv_b, (channels,))
+    if reset is not None:
+        reset = np.ascontiguousarray(np.asarray(reset, dtype=np.uint8))
+        if reset.shape != (batch, L):
+            raise ValueError(f"reset must be [batch, L], got {reset.shape}")
+    x = np.empty((batch, channels, L), dtype=np.float64)
+
+    def run(rng):
+        rc = lib.oracle_conv1d_silu(batch, channels, L, W, _ptr(x_pre), _ptr(conv_w), _ptr(conv_b), _ptr(reset),
+                                    _ptr(x), rng[0], rng[1])
+        if rc != 0:
+            raise ValueError(f"oracle_conv1d_silu rejected its arguments (code {rc})")
+
+    _rows_parallel(batch * channels, threads, run)
+    return x
+
+
+def dt_proj(w_dt, delta, dt_bias=None, apply_softplus=False, threads=None):
+    """dt[b, c, t] = sum_k w_dt[c, k] delta[b, t, k]; with apply_softplus,
+    softplus(dt + dt_bias[c]). w_dt: [channels, R]; delta: [batch, L, R]
+    (token-major). Returns dt [batch, channels, L] in fp64."""
+    lib = _load()
+    w_dt = _f64(w_dt)
+    channels, R = w_dt.shape
+    delta = _f64(delta)
+    if delta.ndim != 3 or delta.shape[2] != R:
+        raise ValueError(f"delta must be [batch, L, {R}], got {delta.shape}")
+    batch, L = delta.shape[:2]
+    dt_bias = _f64(dt_bias, (channels,))
+    dt = np.empty((batch, channels, L), dtype=np.float64)
+
+    def run(rng):
+        rc = lib.oracle_dt_proj(batch, channels, L, R, _ptr(w_dt), _ptr(delta), _ptr(dt_bias),
+                                int(bool(apply_softplus)), _ptr(dt), rng[0], rng[1])
+        if rc != 0:
+            raise ValueError(f"oracle_dt_proj rejected its arguments (code {rc})")
+
+    _rows_parallel(batch * channels, threads, run)
+    return dt

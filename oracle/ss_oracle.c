@@ -236,3 +236,66 @@ int oracle_effective_attention(int64_t batch, int64_t channels, int64_t N, int64
     free(d);
     return ORACLE_OK;
 }
+
+/*
+ * Input side of the scan (nnterp "selective_scan" page, class docstring: the
+ * scan's x is the causal conv1d output after SiLU, and its dt the dt_proj
+ * output; TransformerLens "ssm_mixer" page: x is the post-conv SiLU input,
+ * dt is read from dt_proj's output).
+ *
+ * Depthwise causal convolution of width W over the sequence, then SiLU:
+ *   x[b, c, t] = silu(conv_b[c] + sum_{k=0}^{W-1} conv_w[c, k] * x_pre[b, c, t - (W-1) + k])
+ * where a tap reading a position before 0, or before the first token of the
+ * current document when a reset mask is given (reset[b, s] != 0 marks a
+ * document's first token), reads 0: a document's convolution does not see
+ * the previous document. conv_b may be NULL (= 0), reset NULL (one document).
+ *   x_pre, x : [batch, channels, L];  conv_w : [channels, W];  reset : [batch, L]
+ * Rows r = b * channels + c in [row_begin, row_end).
+ */
+int oracle_conv1d_silu(int64_t batch, int64_t channels, int64_t L, int64_t W,
+                       const double* x_pre, const double* conv_w, const double* conv_b,
+                       const uint8_t* reset, double* x, int64_t row_begin, int64_t row_end) {
+    if (batch < 0 || channels < 0 || L < 0 || W < 1) return ORACLE_BAD_ARG;
+    if (!x_pre || !conv_w || !x) return ORACLE_BAD_ARG;
+    if (row_begin < 0 || row_end > batch * channels || row_begin > row_end) return ORACLE_BAD_ARG;
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const int64_t b = r / channels, c = r % channels;
+        int64_t doc_start = 0;
+        for (int64_t t = 0; t < L; ++t) {
+            if (reset && reset[b * L + t]) doc_start = t;
+            double acc = conv_b ? conv_b[c] : 0.0;
+            for (int64_t k = 0; k < W; ++k) {
+                const int64_t s = t - (W - 1) + k;
+                if (s >= doc_start) acc += conv_w[c * W + k] * x_pre[r * L + s];
+            }
+            x[r * L + t] = silu(acc);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * dt_proj: the step sizes from the low-rank projection,
+ *   dt[b, c, t] = sum_{k=0}^{R-1} w_dt[c, k] * delta[b, t, k]
+ * and, with apply nonzero, dt <- softplus(dt + dt_bias[c]) (dt_bias NULL = 0),
+ * the step size the scan would otherwise form from it.
+ *   w_dt : [channels, R];  delta : [batch, L, R] (token-major, as the
+ *   projection of the tokens produces it);  dt : [batch, channels, L]
+ * Rows r = b * channels + c in [row_begin, row_end).
+ */
+int oracle_dt_proj(int64_t batch, int64_t channels, int64_t L, int64_t R,
+                   const double* w_dt, const double* delta, const double* dt_bias, int apply,
+                   double* dt, int64_t row_begin, int64_t row_end) {
+    if (batch < 0 || channels < 0 || L < 0 || R < 1) return ORACLE_BAD_ARG;
+    if (!w_dt || !delta || !dt) return ORACLE_BAD_ARG;
+    if (row_begin < 0 || row_end > batch * channels || row_begin > row_end) return ORACLE_BAD_ARG;
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const int64_t b = r / channels, c = r % channels;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < R; ++k) acc += w_dt[c * R + k] * delta[(b * L + t) * R + k];
+            dt[r * L + t] = apply ? oracle_softplus(acc + (dt_bias ? dt_bias[c] : 0.0)) : acc;
+        }
+    }
+    return ORACLE_OK;
+}

@@ -12,6 +12,7 @@ import pytest
 import oracle
 from tests import test_oracle_attention_pins as apins
 from tests import test_oracle_gated_pins as gpins
+from tests import test_oracle_producer_pins as ppins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
@@ -62,6 +63,17 @@ MUTANTS = {
     "attn_B_C_swapped": ("Cb[n * L + i] * prod[n] * Bb[n * L + j]", "Bb[n * L + i] * prod[n] * Cb[n * L + j]"),
     "attn_not_causal": ("i >= j ? Cb[n * L + i]", "1 ? Cb[n * L + i]"),
     "attn_row_scaled": ("Bb[n * L + j] * colscale", "Bb[n * L + j] * (include_dt ? d[i] : 1.0)"),
+    # input-side producers
+    "conv_taps_reversed": ("acc += conv_w[c * W + k] * x_pre[r * L + s];",
+                           "acc += conv_w[c * W + (W - 1 - k)] * x_pre[r * L + s];"),
+    "conv_off_by_one": ("const int64_t s = t - (W - 1) + k;", "const int64_t s = t - W + k;"),
+    "conv_reset_ignored": ("if (reset && reset[b * L + t]) doc_start = t;", "if (0) doc_start = t;"),
+    "conv_bias_dropped": ("double acc = conv_b ? conv_b[c] : 0.0;", "double acc = 0.0;"),
+    "conv_no_silu": ("x[r * L + t] = silu(acc);", "x[r * L + t] = acc;"),
+    "dtproj_delta_index": ("acc += w_dt[c * R + k] * delta[(b * L + t) * R + k];",
+                           "acc += w_dt[c * R + k] * delta[(b * L + (L - 1 - t)) * R + k];"),
+    "dtproj_bias_outside_softplus": ("oracle_softplus(acc + (dt_bias ? dt_bias[c] : 0.0))",
+                                     "oracle_softplus(acc) + (dt_bias ? dt_bias[c] : 0.0)"),
 }
 
 
@@ -95,6 +107,16 @@ def _pin_callables():
             calls.append((name, lambda fn=fn: fn(True)))
         else:
             calls.append((name, fn))
+    for name in dir(ppins):
+        if not name.startswith("test_ppin"):
+            continue
+        fn = getattr(ppins, name)
+        if name == "test_ppin1_matches_numpy_convolve":
+            calls.append((name, lambda fn=fn: fn(4)))
+        elif name == "test_ppin5_dt_proj_matches_numpy_matmul":
+            calls.append((name, lambda fn=fn: fn(True)))
+        else:
+            calls.append((name, fn))
     return calls
 
 
@@ -118,7 +140,7 @@ def test_pins_catch_mutant(mutant, monkeypatch):
         so = _build_mutant(old, new, tmp)
         lib = ctypes.CDLL(so)
         for fn in ("oracle_scan", "oracle_update", "oracle_softplus", "oracle_gated_scan",
-                   "oracle_effective_attention"):
+                   "oracle_effective_attention", "oracle_conv1d_silu", "oracle_dt_proj"):
             getattr(lib, fn).restype = getattr(real, fn).restype
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         monkeypatch.setattr(oracle, "_lib", lib)
