@@ -44,16 +44,17 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 5
+#define SS_ABI_VERSION 6
 #define SS_MAX_STATE_DIM 64
 #define SS_MAX_GATED_DK 256
+#define SS_MAX_CONV_WIDTH 8
 
 typedef enum {
   SS_OK = 0,
   SS_ERR_NULL = 1,        /* a required pointer is NULL */
   SS_ERR_SHAPE = 2,       /* a size is negative or an index would overflow */
   SS_ERR_DTYPE = 3,       /* io_dtype is not an ss_dtype */
-  SS_ERR_UNSUPPORTED = 4, /* state_dim outside [1, SS_MAX_STATE_DIM]; gated scan: dk, dv */
+  SS_ERR_UNSUPPORTED = 4, /* state_dim outside [1, SS_MAX_STATE_DIM]; gated scan: dk, dv; conv width; rank */
   SS_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap */
   SS_ERR_HIP = 6,         /* the HIP runtime failed to launch the kernel */
   SS_ERR_ALIGN = 7        /* a pointer is not aligned to its element size */
@@ -205,6 +206,57 @@ int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_
 int ss_effective_attention(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
                            const void* dt, const float* A, const void* B, const void* C, const float* dt_bias,
                            int dt_softplus, int include_dt_scaling, int per_state_coord, float* M, void* stream);
+
+/*
+ * Input side of the scan (nnterp "selective_scan" page, class docstring: the
+ * scan's x is the causal conv1d output after SiLU and its dt the dt_proj
+ * output; TransformerLens "ssm_mixer" page: x is the post-conv SiLU input).
+ *
+ * ss_conv1d_silu: depthwise causal convolution of width W over the sequence,
+ * then SiLU, in fp32:
+ *
+ *   x[b, c, t] = silu(conv_b[c] + sum_{k<W} conv_w[c, k] * x_pre[b, c, t - (W-1) + k])
+ *
+ * A tap before position 0 reads 0, and with a reset mask so does a tap
+ * before the first token of the current document (reset[b, s] != 0 marks a
+ * document's first token, as in ss_scan_fwd): documents packed in one row do
+ * not see each other.
+ *
+ *   x_pre, x    : [batch, channels, seqlen]  io_dtype (x rounded to nearest
+ *                 even for bf16)
+ *   conv_w      : [channels, width] float32; width in [1, SS_MAX_CONV_WIDTH]
+ *   conv_b      : [channels] float32, or NULL (= 0)
+ *   reset       : [batch, seqlen] uint8, or NULL
+ */
+int ss_conv1d_silu(int64_t batch, int64_t channels, int64_t seqlen, int64_t width, int io_dtype,
+                   const void* x_pre, const float* conv_w, const float* conv_b, const uint8_t* reset,
+                   void* x, void* stream);
+
+/*
+ * ss_dt_proj: the step sizes from the low-rank projection, fp32 accumulation
+ * on the matrix cores:
+ *
+ *   dt[b, c, t] = sum_{k<rank} w_dt[c, k] * delta[b, t, k]
+ *
+ * and with apply_softplus nonzero dt <- softplus(dt + dt_bias[c]) (dt_bias
+ * NULL = 0), the step size ss_scan_fwd would otherwise form (then call the
+ * scan with dt_softplus = 0 and no dt_bias).
+ *
+ *   w_dt        : [channels, rank]          io_dtype
+ *   delta       : [batch, seqlen, rank]     io_dtype (token-major, as the
+ *                 projection of the tokens produces it)
+ *   dt_bias     : [channels] float32, or NULL
+ *   dt          : output [batch, channels, seqlen] io_dtype
+ *
+ * For both calls: rank >= 1 (else SS_ERR_UNSUPPORTED); batch, channels or
+ * seqlen == 0 is a no-op returning SS_OK; outputs must not overlap inputs
+ * (SS_ERR_ALIAS). Conventions of the other calls hold (device pointers,
+ * asynchronous on `stream`, validation before any launch, inputs untouched,
+ * bitwise reproducible).
+ */
+int ss_dt_proj(int64_t batch, int64_t channels, int64_t seqlen, int64_t rank, int io_dtype,
+               const void* w_dt, const void* delta, const float* dt_bias, int apply_softplus,
+               void* dt, void* stream);
 
 /* Static, NUL-terminated name of a status code (unknown codes included). */
 const char* ss_status_str(int status);

@@ -19,6 +19,12 @@ and the scalar-gated state scan of the "Mamba 2 Gated State Scan" page:
 
     ss_gated_scan(q, k, v, gamma, s0=None) -> (y, final_state)
 
+the producers of the scan's inputs (the causal conv1d + SiLU that makes x,
+and the dt_proj projection that makes dt):
+
+    ss_conv1d_silu(x_pre, conv_w, conv_b=None, reset=None) -> x
+    ss_dt_proj(w_dt, delta, dt_bias=None, apply_softplus=False) -> dt
+
 and the scan's effective attention of the TransformerLens "ssm_mixer" page:
 
     ss_effective_attention(dt, A, B, C, dt_bias=None, include_dt_scaling=False,
@@ -34,6 +40,8 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     SSError,
     abi_version,
+    ss_conv1d_silu,
+    ss_dt_proj,
     ss_effective_attention,
     ss_gated_scan,
     library_path,

@@ -48,6 +48,10 @@ def load_library() -> ctypes.CDLL:
     lib.ss_gated_scan.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 7 + [vp]
     lib.ss_effective_attention.restype = i32
     lib.ss_effective_attention.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.ss_conv1d_silu.restype = i32
+    lib.ss_conv1d_silu.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.ss_dt_proj.restype = i32
+    lib.ss_dt_proj.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp]
     lib.ss_state_update.restype = i32
     lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
     lib.ss_status_str.restype = ctypes.c_char_p
@@ -284,6 +288,73 @@ def ss_effective_attention(dt, A, B, C, dt_bias=None, *, dt_softplus: bool = Tru
                                                _ptr(out), _stream_handle(dev, stream))
     if rc != SS_OK:
         raise SSError(rc, "ss_effective_attention")
+    return out
+
+
+def ss_conv1d_silu(x_pre, conv_w, conv_b=None, reset=None, *, out=None, stream=None):
+    """x = silu(causal depthwise conv1d of x_pre + conv_b) on the GPU.
+    x_pre: [batch, channels, seq] float32 or bfloat16; conv_w: [channels,
+    width] float32 (width <= 8; conv_w[:, -1] meets the current token);
+    conv_b: [channels] float32 or None; reset: [batch, seq] bool/uint8 or
+    None (a document's taps stop at its first token). Returns x like x_pre."""
+    import torch
+    if x_pre.dim() != 3 or conv_w.dim() != 2:
+        raise ValueError("x_pre must be [batch, channels, seq] and conv_w [channels, width]")
+    batch, channels, L = x_pre.shape
+    dev = x_pre.device
+    if dev.type != "cuda":
+        raise ValueError("ss_conv1d_silu runs on the GPU: x_pre must be a device tensor")
+    io = x_pre.dtype
+    code = _io_code(io)
+    x_pre, conv_w = x_pre.contiguous(), conv_w.contiguous()
+    _check(conv_w, "conv_w", (channels, conv_w.shape[1]), torch.float32, dev)
+    if conv_b is not None:
+        conv_b = conv_b.contiguous()
+        _check(conv_b, "conv_b", (channels,), torch.float32, dev)
+    if reset is not None:
+        reset = reset.to(torch.uint8).contiguous()
+        _check(reset, "reset", (batch, L), torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(x_pre)
+    else:
+        _check(out, "out", (batch, channels, L), io, dev)
+    rc = load_library().ss_conv1d_silu(batch, channels, L, conv_w.shape[1], code, _ptr(x_pre), _ptr(conv_w),
+                                       _ptr(conv_b), _ptr(reset), _ptr(out), _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_conv1d_silu")
+    return out
+
+
+def ss_dt_proj(w_dt, delta, dt_bias=None, *, apply_softplus: bool = False, out=None, stream=None):
+    """dt[b, c, t] = sum_k w_dt[c, k] delta[b, t, k] on the GPU's matrix cores
+    (fp32 accumulation), optionally softplus(dt + dt_bias[c]). w_dt:
+    [channels, rank]; delta: [batch, seq, rank] (token-major), one dtype
+    (float32 or bfloat16); dt_bias: [channels] float32 or None. Returns dt
+    [batch, channels, seq] in that dtype."""
+    import torch
+    if w_dt.dim() != 2 or delta.dim() != 3:
+        raise ValueError("w_dt must be [channels, rank] and delta [batch, seq, rank]")
+    channels, R = w_dt.shape
+    batch, L = delta.shape[:2]
+    dev = delta.device
+    if dev.type != "cuda":
+        raise ValueError("ss_dt_proj runs on the GPU: delta must be a device tensor")
+    io = delta.dtype
+    code = _io_code(io)
+    w_dt, delta = w_dt.contiguous(), delta.contiguous()
+    _check(w_dt, "w_dt", (channels, R), io, dev)
+    _check(delta, "delta", (batch, L, R), io, dev)
+    if dt_bias is not None:
+        dt_bias = dt_bias.contiguous()
+        _check(dt_bias, "dt_bias", (channels,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, channels, L), dtype=io, device=dev)
+    else:
+        _check(out, "out", (batch, channels, L), io, dev)
+    rc = load_library().ss_dt_proj(batch, channels, L, R, code, _ptr(w_dt), _ptr(delta), _ptr(dt_bias),
+                                   int(bool(apply_softplus)), _ptr(out), _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_dt_proj")
     return out
 
 

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssscan.so")
 ARCH = "gfx950"
 
-SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip"]
+SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -1,0 +1,257 @@
+// Input-side producers of the scan for gfx950 (nnterp "selective_scan" page,
+// class docstring: the scan's x is the causal conv1d output after SiLU and
+// its dt the dt_proj output; TransformerLens "ssm_mixer" page: x is the
+// post-conv SiLU input, dt is read from dt_proj's output).
+//
+// conv1d_silu: x[b, c, t] = silu(conv_b[c] + sum_k conv_w[c, k] x_pre[b, c, t - (W-1) + k]),
+// a depthwise causal convolution of width W <= 8; a tap before position 0 or
+// before the current document's first token (reset[b, s] != 0) reads 0.
+// Bound by HBM (one read of x_pre, one write of x). A thread makes 8
+// consecutive tokens of one row from 16 elements (its 8 and the 8 before
+// them, for the taps), with 16-byte loads and stores where rows allow.
+//
+// dt_proj: dt[b, c, t] = sum_k w_dt[c, k] delta[b, t, k] (optionally
+// softplus(dt + dt_bias[c])), a GEMM of channels x tokens over the rank k on
+// the matrix cores: bf16 16x16x32 MFMAs for bf16 I/O, fp32 16x16x4 for fp32.
+// Both operands are contiguous in k (w_dt row-major [channels, R], delta
+// token-major [batch, L, R]), so each lane loads its operand slice with one
+// 16-byte load per 32 (bf16) or 16 (fp32) values of k, straight from L2
+// (w_dt and delta are small next to the dt it writes). Bound by writing dt.
+#include "ss_device.h"
+#include "ss_launch.h"
+
+namespace ss {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------ conv1d + SiLU
+constexpr int kConvTok = 8;        // tokens per thread
+constexpr int kConvThreads = 256;
+constexpr int kMaxWidth = 8;
+
+template <typename IoT, bool VEC>
+__global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(const ConvParams p) {
+  const int64_t L = p.L;
+  const int64_t chunks = (L + kConvTok - 1) / kConvTok;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x;
+  if (g >= p.rows * chunks) return;
+  const int64_t row = g / chunks;               // b * channels + c
+  const int64_t t0 = (g - row * chunks) * kConvTok;
+  const int64_t b = row / p.channels, c = row - b * p.channels;
+  const IoT* __restrict__ xp = static_cast<const IoT*>(p.x_pre) + row * L;
+  const int W = p.W;
+
+  // v[u] = x_pre at t0 - 8 + u, u in [0, 16); positions outside [0, L) are 0
+  float v[2 * kConvTok];
+  if constexpr (VEC) {
+    // rows are whole 16-byte vectors and t0 is a multiple of 8
+    if constexpr (sizeof(IoT) == 2) {
+      u32x4 cur = *reinterpret_cast<const u32x4*>(xp + t0);
+      u32x4 prev = t0 > 0 ? *reinterpret_cast<const u32x4*>(xp + t0 - kConvTok) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pw = prev[e], cw = cur[e];
+        v[2 * e] = __builtin_bit_cast(float, pw << 16);
+        v[2 * e + 1] = __builtin_bit_cast(float, pw & 0xffff0000u);
+        v[kConvTok + 2 * e] = __builtin_bit_cast(float, cw << 16);
+        v[kConvTok + 2 * e + 1] = __builtin_bit_cast(float, cw & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4f cur = *reinterpret_cast<const v4f*>(xp + t0 + 4 * h);
+        const v4f prev = t0 > 0 ? *reinterpret_cast<const v4f*>(xp + t0 - kConvTok + 4 * h) : v4f{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[4 * h + e] = prev[e];
+          v[kConvTok + 4 * h + e] = cur[e];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2 * kConvTok; ++u) {
+      const int64_t s = t0 - kConvTok + u;
+      v[u] = (s >= 0 && s < L) ? Io<IoT>::to_f32(xp[s]) : 0.0f;
+    }
+  }
+  // reset flags of the same 16 positions (1 = a document starts there)
+  bool start[2 * kConvTok];
+#pragma unroll
+  for (int u = 0; u < 2 * kConvTok; ++u) {
+    const int64_t s = t0 - kConvTok + u;
+    start[u] = p.reset && s >= 0 && s < L && p.reset[b * L + s] != 0;
+  }
+  // wr[m]: the weight of the tap m tokens back (conv_w[c, W - 1 - m]), 0 past W
+  float wr[kMaxWidth];
+#pragma unroll
+  for (int m = 0; m < kMaxWidth; ++m) wr[m] = m < W ? p.conv_w[c * W + (W - 1 - m)] : 0.0f;
+  const float bias = p.conv_b ? p.conv_b[c] : 0.0f;
+
+  float out[kConvTok];
+#pragma unroll
+  for (int u = 0; u < kConvTok; ++u) {
+    // token t0 + u is v[8 + u]; the tap m tokens back reads v[8 + u - m],
+    // until a document start has been passed (weights past W are 0)
+    float acc = bias;
+    bool open = true;
+#pragma unroll
+    for (int m = 0; m < kMaxWidth; ++m) {
+      acc = open ? __builtin_fmaf(wr[m], v[kConvTok + u - m], acc) : acc;
+      open = open && !start[kConvTok + u - m];
+    }
+    out[u] = silu_f32(acc);
+  }
+  IoT* __restrict__ xo = static_cast<IoT*>(p.x) + row * L;
+  if constexpr (VEC) {
+    if constexpr (sizeof(IoT) == 2) {
+      store_vec16(reinterpret_cast<bf16_t*>(xo + t0), out);
+    } else {
+      store_vec16(reinterpret_cast<float*>(xo + t0), out);
+      store_vec16(reinterpret_cast<float*>(xo + t0 + 4), out + 4);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kConvTok; ++u)
+      if (t0 + u < L) xo[t0 + u] = Io<IoT>::from_f32(out[u]);
+  }
+}
+
+// ------------------------------------------------------------------ dt_proj
+constexpr int kProjThreads = 256;   // 4 waves
+constexpr int kProjC = 64;          // channels per block: 16 per wave
+constexpr int kProjT = 64;          // tokens per block: 4 MFMA tiles per wave
+
+// One K chunk of operands for lane (row, G): 16 bytes = 8 bf16 or 4 fp32 values
+template <typename IoT, bool VEC>
+__device__ __forceinline__ u32x4 load_k16(const IoT* base, int64_t k0, int64_t R, bool row_ok) {
+  constexpr int E = 16 / sizeof(IoT);
+  if constexpr (VEC) {
+    return (row_ok && k0 < R) ? *reinterpret_cast<const u32x4*>(base + k0) : u32x4{0, 0, 0, 0};
+  } else {
+    u32x4 r = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool in = row_ok && k0 + e < R;
+      if constexpr (sizeof(IoT) == 2) {
+        const uint32_t bits = in ? static_cast<const bf16_t*>(static_cast<const void*>(base))[k0 + e].bits : 0u;
+        r[e >> 1] |= (e & 1) ? (bits << 16) : bits;
+      } else {
+        const float f = in ? base[k0 + e] : 0.0f;
+        r[e] = __builtin_bit_cast(uint32_t, f);
+      }
+    }
+    return r;
+  }
+}
+
+template <typename IoT, bool VEC, bool APPLY>
+__global__ __launch_bounds__(kProjThreads) void dt_proj_kernel(const ProjParams p) {
+  constexpr int KC = sizeof(IoT) == 2 ? 32 : 16;   // k per 16-byte lane load x 4 lane groups
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, r16 = l & 15;
+  const int64_t L = p.L, C = p.channels, R = p.R;
+  const int64_t tblocks = (L + kProjT - 1) / kProjT, cblocks = (C + kProjC - 1) / kProjC;
+  int64_t blk = blockIdx.x;
+  const int64_t tb = blk % tblocks; blk /= tblocks;
+  const int64_t cb = blk % cblocks;
+  const int64_t b = blk / cblocks;
+  const int64_t c0 = cb * kProjC + 16 * w;   // this wave's 16 channels
+  const int64_t t0 = tb * kProjT;
+  const IoT* __restrict__ Wg = static_cast<const IoT*>(p.w_dt);
+  const IoT* __restrict__ Dg = static_cast<const IoT*>(p.delta) + b * L * R;
+
+  // A operand rows: channel c0 + r16; B operand columns: token t0 + 16 n + r16
+  const bool c_ok = c0 + r16 < C;
+  const IoT* wrow = Wg + (c_ok ? (c0 + r16) * R : 0);
+  v4f acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  for (int64_t k0 = 0; k0 < R; k0 += KC) {
+    const int64_t kl = k0 + (KC / 4) * G;   // this lane group's slice of the chunk
+    const u32x4 a = load_k16<IoT, VEC>(wrow, kl, R, c_ok);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int64_t t = t0 + 16 * n + r16;
+      const bool t_ok = t < L;
+      const u32x4 bv = load_k16<IoT, VEC>(Dg + (t_ok ? t * R : 0), kl, R, t_ok);
+      if constexpr (sizeof(IoT) == 2) {
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bv),
+                                                         acc[n], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t ag = a[g], bg = bv[g];
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag), __builtin_bit_cast(float, bg),
+                                                         acc[n], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // D layout: register r at lane (column r16, G) is row 4 G + r, i.e.
+  // channel c0 + 4 G + r and token t0 + 16 n + r16
+  IoT* __restrict__ out = static_cast<IoT*>(p.dt) + b * C * L;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int64_t t = t0 + 16 * n + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t c = c0 + 4 * G + r;
+      if (c < C && t < L) {
+        float v = acc[n][r];
+        if constexpr (APPLY) v = softplus_f32(v + (p.dt_bias ? p.dt_bias[c] : 0.0f));
+        out[c * L + t] = Io<IoT>::from_f32(v);
+      }
+    }
+  }
+}
+
+template <typename IoT>
+hipError_t launch_conv_io(const ConvParams& p, hipStream_t stream) {
+  const int64_t chunks = (p.L + kConvTok - 1) / kConvTok;
+  const int64_t threads = p.rows * chunks;
+  const int64_t blocks = (threads + kConvThreads - 1) / kConvThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const bool vec = p.L % kConvTok == 0 && reinterpret_cast<uintptr_t>(p.x_pre) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.x) % 16 == 0;
+  void* args[] = {const_cast<ConvParams*>(&p)};
+  const void* fn = vec ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true>)
+                       : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kConvThreads), args, 0, stream);
+}
+
+template <typename IoT, bool VEC>
+hipError_t launch_proj_vec(const ProjParams& p, hipStream_t stream) {
+  const int64_t blocks = p.batch * ((p.channels + kProjC - 1) / kProjC) * ((p.L + kProjT - 1) / kProjT);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  void* args[] = {const_cast<ProjParams*>(&p)};
+  const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_kernel<IoT, VEC, true>)
+                           : reinterpret_cast<const void*>(&dt_proj_kernel<IoT, VEC, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kProjThreads), args, 0, stream);
+}
+
+template <typename IoT>
+hipError_t launch_proj_io(const ProjParams& p, hipStream_t stream) {
+  constexpr int E = 16 / sizeof(IoT);
+  const bool vec = p.R % E == 0 && reinterpret_cast<uintptr_t>(p.w_dt) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.delta) % 16 == 0;
+  return vec ? launch_proj_vec<IoT, true>(p, stream) : launch_proj_vec<IoT, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_silu(const ConvParams& p, bool io_bf16, hipStream_t stream) {
+  return io_bf16 ? launch_conv_io<bf16_t>(p, stream) : launch_conv_io<float>(p, stream);
+}
+
+hipError_t launch_dt_proj(const ProjParams& p, bool io_bf16, hipStream_t stream) {
+  return io_bf16 ? launch_proj_io<bf16_t>(p, stream) : launch_proj_io<float>(p, stream);
+}
+
+bool producer_grids_ok(int64_t batch, int64_t channels, int64_t L) {
+  const int64_t conv_blocks = (batch * channels * ((L + kConvTok - 1) / kConvTok) + kConvThreads - 1) / kConvThreads;
+  const int64_t proj_blocks = batch * ((channels + kProjC - 1) / kProjC) * ((L + kProjT - 1) / kProjT);
+  return conv_blocks <= 0x7fffffff && proj_blocks <= 0x7fffffff;
+}
+
+}  // namespace ss

@@ -161,6 +161,50 @@ int ss_effective_attention(int64_t batch, int64_t channels, int64_t state_dim, i
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
+int ss_conv1d_silu(int64_t batch, int64_t channels, int64_t seqlen, int64_t width, int io_dtype,
+                   const void* x_pre, const float* conv_w, const float* conv_b, const uint8_t* reset,
+                   void* x, void* stream) {
+  const ss::ConvArgs a{batch, channels, seqlen, width, io_dtype, x_pre, conv_w, conv_b, reset, x};
+  bool noop = false;
+  const ss_status st = ss::validate_conv(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (!ss::producer_grids_ok(batch, channels, seqlen)) return SS_ERR_SHAPE;
+  ss::ConvParams p{};
+  p.rows = batch * channels;
+  p.channels = channels;
+  p.L = seqlen;
+  p.W = (int)width;
+  p.x_pre = x_pre;
+  p.conv_w = conv_w;
+  p.conv_b = conv_b;
+  p.reset = reset;
+  p.x = x;
+  const hipError_t e = ss::launch_conv1d_silu(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_dt_proj(int64_t batch, int64_t channels, int64_t seqlen, int64_t rank, int io_dtype,
+               const void* w_dt, const void* delta, const float* dt_bias, int apply_softplus,
+               void* dt, void* stream) {
+  const ss::ProjArgs a{batch, channels, seqlen, rank, io_dtype, w_dt, delta, dt_bias, apply_softplus, dt};
+  bool noop = false;
+  const ss_status st = ss::validate_proj(a, &noop);
+  if (st != SS_OK || noop) return st;
+  if (!ss::producer_grids_ok(batch, channels, seqlen)) return SS_ERR_SHAPE;
+  ss::ProjParams p{};
+  p.batch = batch;
+  p.channels = channels;
+  p.L = seqlen;
+  p.R = rank;
+  p.w_dt = w_dt;
+  p.delta = delta;
+  p.dt_bias = dt_bias;
+  p.apply = apply_softplus != 0;
+  p.dt = dt;
+  const hipError_t e = ss::launch_dt_proj(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
 const char* ss_status_str(int status) {
   switch (status) {
     case SS_OK: return "SS_OK";

@@ -75,6 +75,29 @@ hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t str
 bool scan_rows_supported(const ScanParams& p, bool io_bf16);
 hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
 // The scalar-gated state scan (gated_scan.hip); io_bf16: element type of q, k, v, y.
+// Input-side producers; see ss_conv1d_silu and ss_dt_proj in ss_scan.h.
+struct ConvParams {
+  int64_t rows, channels, L;   // rows = batch * channels
+  int W;
+  const void* x_pre;           // [batch, channels, L]
+  const float* conv_w;         // [channels, W]
+  const float* conv_b;         // [channels] or nullptr
+  const uint8_t* reset;        // [batch, L] or nullptr
+  void* x;                     // [batch, channels, L]
+};
+
+struct ProjParams {
+  int64_t batch, channels, L, R;
+  const void* w_dt;            // [channels, R]
+  const void* delta;           // [batch, L, R]
+  const float* dt_bias;        // [channels] or nullptr
+  int apply;                   // softplus(dt + dt_bias)
+  void* dt;                    // [batch, channels, L]
+};
+
+hipError_t launch_conv1d_silu(const ConvParams& p, bool io_bf16, hipStream_t stream);
+hipError_t launch_dt_proj(const ProjParams& p, bool io_bf16, hipStream_t stream);
+
 // Effective attention; see ss_effective_attention in ss_scan.h.
 struct AttnParams {
   int64_t batch, channels, L;
@@ -102,4 +125,5 @@ int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
 bool state_update_grid_ok(int64_t batch, int64_t channels, int64_t state_dim);
 int64_t gated_scan_blocks(int64_t batch, int64_t dv);
 int64_t effective_attention_blocks(int64_t batch, int64_t channels, int64_t L);
+bool producer_grids_ok(int64_t batch, int64_t channels, int64_t L);
 }  // namespace ss

@@ -210,6 +210,77 @@ inline ss_status validate_attention(const AttnArgs& a, bool* noop) {
   return SS_OK;
 }
 
+// Inputs of the input-side producers; see ss_conv1d_silu and ss_dt_proj.
+struct ConvArgs {
+  int64_t batch, channels, seqlen, width;
+  int io_dtype;
+  const void* x_pre;
+  const float *conv_w, *conv_b;
+  const uint8_t* reset;
+  void* x;
+};
+
+inline ss_status validate_conv(const ConvArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.channels < 0 || a.seqlen < 0 || a.width < 0) return SS_ERR_SHAPE;
+  if (a.width < 1 || a.width > SS_MAX_CONV_WIDTH) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0 || a.channels == 0 || a.seqlen == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t bc, n, bytes, wn, w_bytes, r_bytes;
+  if (!mul_ok(a.batch, a.channels, &bc) || !mul_ok(bc, a.seqlen, &n) || !mul_ok(n, es, &bytes) ||
+      !mul_ok(a.channels, a.width, &wn) || !mul_ok(wn, 4, &w_bytes) || !mul_ok(a.batch, a.seqlen, &r_bytes))
+    return SS_ERR_SHAPE;
+  if (bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  if (!a.x_pre || !a.conv_w || !a.x) return SS_ERR_NULL;
+  if (!aligned(a.x_pre, es) || !aligned(a.x, es)) return SS_ERR_ALIGN;
+  if (!aligned(a.conv_w, 4) || (a.conv_b && !aligned(a.conv_b, 4))) return SS_ERR_ALIGN;
+  const Span out(a.x, bytes);
+  const Span inputs[] = {Span(a.x_pre, bytes), Span(a.conv_w, w_bytes), Span(a.conv_b, a.channels * 4),
+                         Span(a.reset, r_bytes)};
+  for (const Span& in : inputs)
+    if (out.overlaps(in)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
+struct ProjArgs {
+  int64_t batch, channels, seqlen, rank;
+  int io_dtype;
+  const void *w_dt, *delta;
+  const float* dt_bias;
+  int apply_softplus;
+  void* dt;
+};
+
+inline ss_status validate_proj(const ProjArgs& a, bool* noop) {
+  *noop = false;
+  if (a.io_dtype != SS_F32 && a.io_dtype != SS_BF16) return SS_ERR_DTYPE;
+  if (a.batch < 0 || a.channels < 0 || a.seqlen < 0 || a.rank < 0) return SS_ERR_SHAPE;
+  if (a.rank < 1) return SS_ERR_UNSUPPORTED;
+  if (a.batch == 0 || a.channels == 0 || a.seqlen == 0) {
+    *noop = true;
+    return SS_OK;
+  }
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t bc, n, out_bytes, wn, w_bytes, bl, dn, d_bytes;
+  if (!mul_ok(a.batch, a.channels, &bc) || !mul_ok(bc, a.seqlen, &n) || !mul_ok(n, es, &out_bytes) ||
+      !mul_ok(a.channels, a.rank, &wn) || !mul_ok(wn, es, &w_bytes) || !mul_ok(a.batch, a.seqlen, &bl) ||
+      !mul_ok(bl, a.rank, &dn) || !mul_ok(dn, es, &d_bytes))
+    return SS_ERR_SHAPE;
+  if (out_bytes > (INT64_MAX >> 2) || d_bytes > (INT64_MAX >> 2)) return SS_ERR_SHAPE;
+  if (!a.w_dt || !a.delta || !a.dt) return SS_ERR_NULL;
+  if (!aligned(a.w_dt, es) || !aligned(a.delta, es) || !aligned(a.dt, es)) return SS_ERR_ALIGN;
+  if (a.dt_bias && !aligned(a.dt_bias, 4)) return SS_ERR_ALIGN;
+  const Span out(a.dt, out_bytes);
+  const Span inputs[] = {Span(a.w_dt, w_bytes), Span(a.delta, d_bytes), Span(a.dt_bias, a.channels * 4)};
+  for (const Span& in : inputs)
+    if (out.overlaps(in)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
 // Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
 struct UpdateArgs {
   int64_t batch, channels, state_dim;

@@ -29,6 +29,13 @@ in the order q, k, v, gamma, zero mask, s0: ``q, k ~ N(0, dk^-1/2)``,
 ``v ~ N(0, 1)``; ``gamma ~ Uniform(0.9, 1)`` ("decay"), ``Uniform(0, 1)``
 ("uniform"), or exactly 1 or 0; with ``zero_rate`` each gamma is also set to
 0 with that probability (a state cleared at that token); ``s0 ~ N(0, 1)``.
+
+Input-side producer cases (the conv1d + SiLU that makes x, the dt_proj
+projection that makes dt), drawn in the order x_pre, conv_w, conv_b, w_dt,
+delta, dt_bias, reset: ``x_pre ~ N(0, 1)``, ``conv_w ~ N(0, W^-1/2)``,
+``conv_b ~ N(0, 0.1)``, ``w_dt ~ N(0, R^-1/2)``, ``delta ~ N(0, 1)``
+(token-major [batch, L, R]), ``dt_bias ~ N(-4, 0.5)``, and the packed-reset
+mask recipe above when a mean document length is given.
 """
 from __future__ import annotations
 
@@ -227,3 +234,23 @@ def make_gated_case(seed: int, batch: int, seqlen: int, dk: int, dv: int, io_dty
     out = {"q": q.to(io), "k": k.to(io), "v": v.to(io), "gamma": g.to(torch.float32),
            "s0": None if st is None else st.to(sdt)}
     return {key: None if t is None else t.to(device) for key, t in out.items()}
+
+
+def make_producer_case(seed: int, batch: int, channels: int, seqlen: int, width: int = 4, rank: int = 160,
+                       io_dtype: str = "bf16", reset_mean_doc: Optional[int] = None,
+                       device: str = "cpu") -> Dict[str, Optional[torch.Tensor]]:
+    """A producer case (recipe in the module docstring): keys x_pre, delta,
+    w_dt (io_dtype), conv_w, conv_b, dt_bias (fp32), reset (uint8 or None)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    io = _TORCH_DTYPE[io_dtype]
+    x_pre = _normal(gen, (batch, channels, seqlen))
+    conv_w = _normal(gen, (channels, width), std=width ** -0.5)
+    conv_b = _normal(gen, (channels,), std=0.1)
+    w_dt = _normal(gen, (channels, rank), std=rank ** -0.5)
+    delta = _normal(gen, (batch, seqlen, rank))
+    dt_bias = _normal(gen, (channels,), mean=-4.0, std=0.5)
+    reset = reset_mask(gen, batch, seqlen, reset_mean_doc) if reset_mean_doc is not None else None
+    out = {"x_pre": x_pre.to(io), "conv_w": conv_w, "conv_b": conv_b, "w_dt": w_dt.to(io), "delta": delta.to(io),
+           "dt_bias": dt_bias, "reset": reset}
+    return {k: None if t is None else t.to(device) for k, t in out.items()}

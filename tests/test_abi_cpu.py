@@ -31,8 +31,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["ss_abi_version", "ss_effective_attention", "ss_gated_scan", "ss_scan_fwd",
-                                    "ss_scan_fwd_states", "ss_state_update", "ss_status_str"]
+    assert declared_functions() == ["ss_abi_version", "ss_conv1d_silu", "ss_dt_proj", "ss_effective_attention",
+                                    "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_states", "ss_state_update",
+                                    "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 5
+    assert ss.abi_version() == 6
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -153,6 +154,35 @@ def test_attention_validation(lib):
     assert attn_call(lib, L=1 << 31, channels=1 << 20) == SHAPE  # M's bytes overflow
     assert attn_call(lib, batch=0) == OK
     assert attn_call(lib, L=0) == OK
+
+
+def conv_call(lib, batch=2, channels=3, L=64, W=4, io=1, x_pre=1 * MB, w=2 * MB, b=None, reset=None, x=4 * MB):
+    return lib.ss_conv1d_silu(batch, channels, L, W, io, x_pre, w, b, reset, x, None)
+
+
+def proj_call(lib, batch=2, channels=64, L=64, R=16, io=1, w=1 * MB, delta=2 * MB, bias=None, dt=4 * MB):
+    return lib.ss_dt_proj(batch, channels, L, R, io, w, delta, bias, 1, dt, None)
+
+
+def test_producer_validation(lib):
+    assert conv_call(lib, io=9) == DTYPE
+    assert conv_call(lib, W=0) == UNSUP
+    assert conv_call(lib, W=9) == UNSUP
+    assert conv_call(lib, L=-1) == SHAPE
+    assert conv_call(lib, x_pre=None) == NULL
+    assert conv_call(lib, w=None) == NULL
+    assert conv_call(lib, x=4 * MB + 1) == ALIGN
+    assert conv_call(lib, w=2 * MB + 2) == ALIGN
+    assert conv_call(lib, x=1 * MB + 2) == ALIAS        # x over x_pre
+    assert conv_call(lib, reset=4 * MB + 100) == ALIAS  # reset inside x
+    assert conv_call(lib, batch=0) == OK
+    assert proj_call(lib, io=9) == DTYPE
+    assert proj_call(lib, R=0) == UNSUP
+    assert proj_call(lib, delta=None) == NULL
+    assert proj_call(lib, dt=4 * MB + 1) == ALIGN
+    assert proj_call(lib, bias=3 * MB + 2) == ALIGN
+    assert proj_call(lib, dt=2 * MB) == ALIAS           # dt over delta
+    assert proj_call(lib, L=0) == OK
 
 
 def test_update_validation(lib):
