@@ -64,7 +64,7 @@ def parse():
                     help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the per-token-states, gated-scan and effective-attention measurements")
+                    help="skip the per-token-states, gated-scan, effective-attention and producer measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
@@ -242,6 +242,47 @@ def measure_attention(ss, stream, reps: int = 20):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+PRODUCER_SHAPE = (8, 5120, 2048, 4, 160)   # batch, channels, seq, conv width, dt rank
+
+
+def measure_producers(ss, stream, reps: int = 20):
+    """The scan's input side at the Mamba-2.8B layer shape (batch 8, channels
+    5120, seq 2048, bf16): ss_conv1d_silu (width 4; bytes: read x_pre, write
+    x) and ss_dt_proj (rank 160, with bias and softplus; bytes: read w_dt and
+    delta, write dt; flops 2 R per output). Per-launch HIP-event averages."""
+    import torch
+    from selective_state_space_ss_amd.workloads import make_producer_case
+    batch, channels, L, W, R = PRODUCER_SHAPE
+    c = make_producer_case(1030, batch, channels, L, W, R, "bf16", device="cuda")
+    x = torch.empty_like(c["x_pre"])
+    dt = torch.empty(batch, channels, L, dtype=torch.bfloat16, device="cuda")
+    calls = {
+        "ss_conv1d_silu": (lambda: ss.ss_conv1d_silu(c["x_pre"], c["conv_w"], c["conv_b"], out=x),
+                           2 * batch * channels * L * 2 + channels * (W + 1) * 4, 0.0),
+        "ss_dt_proj": (lambda: ss.ss_dt_proj(c["w_dt"], c["delta"], c["dt_bias"], apply_softplus=True, out=dt),
+                       batch * channels * L * 2 + batch * L * R * 2 + channels * R * 2 + channels * 4,
+                       2.0 * batch * channels * L * R),
+    }
+    res = {"shape": {"batch": batch, "channels": channels, "seq": L, "width": W, "rank": R, "io": "bf16"}}
+    for name, (f, nbytes, flops) in calls.items():
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        r = {"us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        if flops:
+            r["TFLOP_s"] = round(flops / (us * 1e-6) / 1e12, 2)
+        res[name] = r
+    return res
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """The oracle over whole (b, c) rows of the prompt workload, row blocks of
     every batch row in turn, until the time budget is spent."""
@@ -403,7 +444,8 @@ def main():
     if not args.no_extras:
         out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream),
                          "ss_gated_scan": measure_gated(ss, stream),
-                         "ss_effective_attention": measure_attention(ss, stream)}
+                         "ss_effective_attention": measure_attention(ss, stream),
+                         "producers": measure_producers(ss, stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -17,6 +17,8 @@
 // token-major [batch, L, R]), so each lane loads its operand slice with one
 // 16-byte load per 32 (bf16) or 16 (fp32) values of k, straight from L2
 // (w_dt and delta are small next to the dt it writes). Bound by writing dt.
+// Ranks of up to 8 chunks with whole 16-byte rows take the streaming form
+// below; other shapes a plain tile-per-block form.
 #include "ss_device.h"
 #include "ss_launch.h"
 
@@ -206,6 +208,138 @@ __global__ __launch_bounds__(kProjThreads) void dt_proj_kernel(const ProjParams 
   }
 }
 
+// Streaming form for ranks up to 8 chunks (R <= 256 bf16, 128 fp32) with
+// whole 16-byte rows: a block owns 64 channels of one batch row, keeps their
+// w_dt operand slices in registers, and walks the sequence in 64-token
+// tiles. Each tile of delta ([token][k], k contiguous) is loaded with 16-byte
+// loads one tile ahead into registers, written to one of two LDS buffers and
+// read back as MFMA B operands; the 64 x 64 output tile goes through LDS so
+// that every row of 64 tokens is written with whole 16-byte stores.
+constexpr int kStreamT = 64;
+
+template <typename IoT, int KCH>
+struct ProjStage {
+  static constexpr int E = 16 / sizeof(IoT);
+  static constexpr int KP = KCH * 4 * E + E;   // k per staged row, padded by one vector
+  IoT d[2][kStreamT][KP];
+  IoT o[kProjC][kStreamT + E];
+};
+
+template <typename IoT, int KCH, bool APPLY>
+__global__ __launch_bounds__(kProjThreads) void dt_proj_stream_kernel(const ProjParams p) {
+  using St = ProjStage<IoT, KCH>;
+  constexpr int E = St::E;
+  constexpr int KC = 4 * E;                      // k per MFMA chunk
+  constexpr int RV = KCH * 4;                    // 16-byte vectors per staged row
+  constexpr int TV = kStreamT * RV;              // vectors per tile
+  constexpr int NPF = (TV + kProjThreads - 1) / kProjThreads;
+  __shared__ __align__(16) St st;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, r16 = l & 15;
+  const int64_t L = p.L, C = p.channels, R = p.R;
+  const int64_t cblocks = (C + kProjC - 1) / kProjC;
+  const int64_t b = blockIdx.x / cblocks;
+  const int64_t cbase = (blockIdx.x - b * cblocks) * kProjC;
+  const int64_t c0 = cbase + 16 * w;
+  const IoT* __restrict__ Dg = static_cast<const IoT*>(p.delta) + b * L * R;
+  IoT* __restrict__ out = static_cast<IoT*>(p.dt) + b * C * L;
+
+  // this wave's A operands: w_dt[c0 + r16][kc * KC + E * G .. + E - 1]
+  u32x4 a[KCH];
+  {
+    const bool c_ok = c0 + r16 < C;
+    const IoT* wrow = static_cast<const IoT*>(p.w_dt) + (c_ok ? (c0 + r16) * R : 0);
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) a[kc] = load_k16<IoT, true>(wrow, kc * KC + E * G, R, c_ok);
+  }
+  float bias[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t c = c0 + 4 * G + r;
+    bias[r] = (APPLY && p.dt_bias && c < C) ? p.dt_bias[c] : 0.0f;
+  }
+
+  u32x4 pf[NPF];
+  auto prefetch = [&](int64_t t0) {
+#pragma unroll
+    for (int n = 0; n < NPF; ++n) {
+      const int e = tid + n * kProjThreads;
+      const int t = e / RV, kv = (e - t * RV) * E;
+      const bool in = e < TV && t0 + t < L && kv < R;
+      pf[n] = in ? *reinterpret_cast<const u32x4*>(Dg + (t0 + t) * R + kv) : u32x4{0, 0, 0, 0};
+    }
+  };
+  const int64_t ntiles = (L + kStreamT - 1) / kStreamT;
+  if (ntiles > 0) prefetch(0);
+  for (int64_t it = 0; it < ntiles; ++it) {
+    const int64_t t0 = it * kStreamT;
+    const int buf = static_cast<int>(it & 1);
+#pragma unroll
+    for (int n = 0; n < NPF; ++n) {
+      const int e = tid + n * kProjThreads;
+      if (e < TV) {
+        const int t = e / RV, kv = (e - t * RV) * E;
+        *reinterpret_cast<u32x4*>(&st.d[buf][t][kv]) = pf[n];
+      }
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) prefetch(t0 + kStreamT);
+    v4f acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * n + r16][kc * KC + E * G]);
+        if constexpr (sizeof(IoT) == 2) {
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[kc]),
+                                                           __builtin_bit_cast(bf16x8, bv), acc[n], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t ag = a[kc][g], bg = bv[g];
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag),
+                                                           __builtin_bit_cast(float, bg), acc[n], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // D: register r at lane (r16, G) of tile n is channel 16 w + 4 G + r,
+    // token 16 n + r16 of the tile
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[n][r];
+        if constexpr (APPLY) v = softplus_f32(v + bias[r]);
+        st.o[16 * w + 4 * G + r][16 * n + r16] = Io<IoT>::from_f32(v);
+      }
+    __syncthreads();
+    // rows of 64 tokens, E per 16-byte store
+    constexpr int OV = kStreamT / E;               // vectors per output row
+    for (int e = tid; e < kProjC * OV; e += kProjThreads) {
+      const int cl = e / OV, tv = (e - cl * OV) * E;
+      const int64_t c = cbase + cl, t = t0 + tv;
+      if (c < C && t < L) {
+        if (t + E <= L) {
+          *reinterpret_cast<u32x4*>(out + c * L + t) = *reinterpret_cast<const u32x4*>(&st.o[cl][tv]);
+        } else {
+          for (int x = 0; x < E && t + x < L; ++x) out[c * L + t + x] = st.o[cl][tv + x];
+        }
+      }
+    }
+  }
+}
+
+template <typename IoT, int KCH>
+hipError_t launch_stream(const ProjParams& p, hipStream_t stream) {
+  const int64_t blocks = p.batch * ((p.channels + kProjC - 1) / kProjC);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  void* args[] = {const_cast<ProjParams*>(&p)};
+  const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_stream_kernel<IoT, KCH, true>)
+                           : reinterpret_cast<const void*>(&dt_proj_stream_kernel<IoT, KCH, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kProjThreads), args, 0, stream);
+}
+
 template <typename IoT>
 hipError_t launch_conv_io(const ConvParams& p, hipStream_t stream) {
   const int64_t chunks = (p.L + kConvTok - 1) / kConvTok;
@@ -233,8 +367,24 @@ hipError_t launch_proj_vec(const ProjParams& p, hipStream_t stream) {
 template <typename IoT>
 hipError_t launch_proj_io(const ProjParams& p, hipStream_t stream) {
   constexpr int E = 16 / sizeof(IoT);
+  constexpr int KC = 4 * E;
   const bool vec = p.R % E == 0 && reinterpret_cast<uintptr_t>(p.w_dt) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(p.delta) % 16 == 0;
+  // the streaming kernel also needs whole 16-byte output rows
+  const bool rows16 = p.L % E == 0 && reinterpret_cast<uintptr_t>(p.dt) % 16 == 0;
+  const int64_t kch = (p.R + KC - 1) / KC;
+  if (vec && rows16 && kch <= 8) {
+    switch (kch) {
+      case 1: return launch_stream<IoT, 1>(p, stream);
+      case 2: return launch_stream<IoT, 2>(p, stream);
+      case 3: return launch_stream<IoT, 3>(p, stream);
+      case 4: return launch_stream<IoT, 4>(p, stream);
+      case 5: return launch_stream<IoT, 5>(p, stream);
+      case 6: return launch_stream<IoT, 6>(p, stream);
+      case 7: return launch_stream<IoT, 7>(p, stream);
+      default: return launch_stream<IoT, 8>(p, stream);
+    }
+  }
   return vec ? launch_proj_vec<IoT, true>(p, stream) : launch_proj_vec<IoT, false>(p, stream);
 }
 

@@ -81,6 +81,9 @@ PROJ_CASES = [
     ("bf16", 1, 65, 33, 20, True),
     ("f32", 1, 16, 16, 7, False),
     ("f32", 1, 33, 130, 64, True),
+    ("bf16", 1, 100, 200, 64, True),     # streaming form: channel and token tails
+    ("f32", 2, 64, 96, 128, False),      # streaming form: 8 chunks of k
+    ("bf16", 1, 70, 72, 256, True),
 ]
 
 
