@@ -73,13 +73,17 @@ def parse():
     return ap.parse_args()
 
 
+SCAN_SOURCES = ("scan_fwd.hip", "scan_chunked.h", "ss_device.h", "ss_launch.h")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources the library is built from: a traffic figure
-    is reported only while it matches (the kernel has not changed since)."""
+    """Digest of the sources the prompt-scan kernel is compiled from: a
+    traffic figure is reported only while it matches (the kernel has not
+    changed since the counters were taken)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_ss_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in SCAN_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
