@@ -223,10 +223,12 @@ struct ProjStage {
   static constexpr int KP = KCH * 4 * E + E;   // k per staged row, padded by one vector
   IoT d[2][kStreamT][KP];
   IoT o[kProjC][kStreamT + E];
+  float bias[kProjC];
 };
 
 template <typename IoT, int KCH, bool APPLY>
-__global__ __launch_bounds__(kProjThreads) void dt_proj_stream_kernel(const ProjParams p) {
+__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(KCH <= 5 ? 3 : 1))) void
+dt_proj_stream_kernel(const ProjParams p) {
   using St = ProjStage<IoT, KCH>;
   constexpr int E = St::E;
   constexpr int KC = 4 * E;                      // k per MFMA chunk
@@ -235,29 +237,29 @@ __global__ __launch_bounds__(kProjThreads) void dt_proj_stream_kernel(const Proj
   constexpr int NPF = (TV + kProjThreads - 1) / kProjThreads;
   __shared__ __align__(16) St st;
 
+  // Wave w computes all 64 channels of the block against tokens
+  // [16 w, 16 w + 16) of each tile: every B operand read from LDS feeds the
+  // four channel tiles' MFMAs, whose A operands stay in registers.
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, r16 = l & 15;
   const int64_t L = p.L, C = p.channels, R = p.R;
   const int64_t cblocks = (C + kProjC - 1) / kProjC;
   const int64_t b = blockIdx.x / cblocks;
   const int64_t cbase = (blockIdx.x - b * cblocks) * kProjC;
-  const int64_t c0 = cbase + 16 * w;
   const IoT* __restrict__ Dg = static_cast<const IoT*>(p.delta) + b * L * R;
   IoT* __restrict__ out = static_cast<IoT*>(p.dt) + b * C * L;
 
-  // this wave's A operands: w_dt[c0 + r16][kc * KC + E * G .. + E - 1]
-  u32x4 a[KCH];
-  {
-    const bool c_ok = c0 + r16 < C;
-    const IoT* wrow = static_cast<const IoT*>(p.w_dt) + (c_ok ? (c0 + r16) * R : 0);
+  // A operands of channel tile m: w_dt[cbase + 16 m + r16][kc * KC + E * G .. + E - 1]
+  u32x4 a[4][KCH];
 #pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) a[kc] = load_k16<IoT, true>(wrow, kc * KC + E * G, R, c_ok);
-  }
-  float bias[4];
+  for (int m = 0; m < 4; ++m) {
+    const int64_t c = cbase + 16 * m + r16;
+    const bool c_ok = c < C;
+    const IoT* wrow = static_cast<const IoT*>(p.w_dt) + (c_ok ? c * R : 0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t c = c0 + 4 * G + r;
-    bias[r] = (APPLY && p.dt_bias && c < C) ? p.dt_bias[c] : 0.0f;
+    for (int kc = 0; kc < KCH; ++kc) a[m][kc] = load_k16<IoT, true>(wrow, kc * KC + E * G, R, c_ok);
   }
+
+  if (APPLY && tid < kProjC) st.bias[tid] = (p.dt_bias && cbase + tid < C) ? p.dt_bias[cbase + tid] : 0.0f;
 
   u32x4 pf[NPF];
   auto prefetch = [&](int64_t t0) {
@@ -287,32 +289,35 @@ __global__ __launch_bounds__(kProjThreads) void dt_proj_stream_kernel(const Proj
     v4f acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
     for (int kc = 0; kc < KCH; ++kc) {
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * w + r16][kc * KC + E * G]);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * n + r16][kc * KC + E * G]);
+      for (int m = 0; m < 4; ++m) {
         if constexpr (sizeof(IoT) == 2) {
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[kc]),
-                                                           __builtin_bit_cast(bf16x8, bv), acc[n], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][kc]),
+                                                           __builtin_bit_cast(bf16x8, bv), acc[m], 0, 0, 0);
         } else {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const uint32_t ag = a[kc][g], bg = bv[g];
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag),
-                                                           __builtin_bit_cast(float, bg), acc[n], 0, 0, 0);
+            const uint32_t ag = a[m][kc][g], bg = bv[g];
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag),
+                                                           __builtin_bit_cast(float, bg), acc[m], 0, 0, 0);
           }
         }
       }
     }
-    // D: register r at lane (r16, G) of tile n is channel 16 w + 4 G + r,
-    // token 16 n + r16 of the tile
+    // D: register r at lane (r16, G) of channel tile m is channel 16 m + 4 G + r,
+    // token 16 w + r16 of the tile
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int m = 0; m < 4; ++m) {
+      v4f bm = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (APPLY) bm = *reinterpret_cast<const v4f*>(&st.bias[16 * m + 4 * G]);  // staged before
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = acc[n][r];
-        if constexpr (APPLY) v = softplus_f32(v + bias[r]);
-        st.o[16 * w + 4 * G + r][16 * n + r16] = Io<IoT>::from_f32(v);
+        float v = acc[m][r];
+        if constexpr (APPLY) v = softplus_f32(v + bm[r]);
+        st.o[16 * m + 4 * G + r][16 * w + r16] = Io<IoT>::from_f32(v);
       }
+    }
     __syncthreads();
     // rows of 64 tokens, E per 16-byte store
     constexpr int OV = kStreamT / E;               // vectors per output row
