@@ -14,7 +14,9 @@
 //   S_new = P_15 S_prev + sum_s L[15][s] k_s v_s^T
 //
 // which is the recurrence unrolled over the chunk (the page's S_t written out
-// from S_prev). Every product is a 16 x 16 x 4 fp32 MFMA.
+// from S_prev). With fp32 I/O every product is a 16 x 16 x 4 fp32 MFMA; with
+// bf16 I/O the products run on the bf16 matrix cores with fp32 accumulation,
+// the fp32 operands split exactly into three bf16 terms (chunk_bf16 below).
 //
 // Layout. A block is one batch item and 64 columns of dv, 4 waves of 16
 // columns each; a wave keeps all dk rows of its columns of S in registers, in
@@ -35,7 +37,9 @@
 // whole 16-byte vectors take a slower element-wise path.
 //
 // Rows of dk past dk, columns past dv and tokens past L are staged as zeros
-// (gamma as 1): they change nothing and are never stored.
+// (gamma as 1): they change nothing and are never stored. A chunk's y goes to
+// LDS and is stored, as whole 16-byte row segments when rows allow, after the
+// next chunk's barrier.
 #include "ss_device.h"
 #include "ss_launch.h"
 
@@ -85,6 +89,126 @@ __device__ __forceinline__ E elem(const u32x4 v, int e) {
 }
 
 
+// ---- bf16 I/O: products on the bf16 matrix cores
+//
+// q, k and v are exact bf16 values, so their products are exact in fp32 and
+// the bf16 MFMAs (fp32 accumulation) compute q k^T as exactly as the fp32
+// ones. The operands that are fp32 (the state for q S, the weighted M for
+// M v, and L[15] v for the state update) are split into three bf16 terms by
+// truncation: hi keeps the top 8 significant bits, mid the next 8 of the
+// exact remainder, lo the rest (at most 8 bits, so exact), and
+// hi + mid + lo is the fp32 value exactly; each term's products with a bf16
+// operand are exact, so the split adds no rounding of its own.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+struct Split4 {
+  u32x2 hi, mid, lo;  // four bf16 values each, two per dword (element 0 low)
+};
+
+__device__ __forceinline__ Split4 split4(const v4f x) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float xe = x[e];
+    const uint32_t hb = __builtin_bit_cast(uint32_t, xe) & 0xffff0000u;
+    const float r = xe - __builtin_bit_cast(float, hb);
+    const uint32_t mb = __builtin_bit_cast(uint32_t, r) & 0xffff0000u;
+    const float r2 = r - __builtin_bit_cast(float, mb);
+    h[e] = hb;
+    m[e] = mb;
+    l[e] = __builtin_bit_cast(uint32_t, r2) & 0xffff0000u;
+  }
+  Split4 o;
+  o.hi = u32x2{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
+  o.mid = u32x2{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
+  o.lo = u32x2{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+  return o;
+}
+
+__device__ __forceinline__ v4f mfma16(const u32x2 a, const u32x2 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0,
+                                                   0);
+}
+__device__ __forceinline__ v4f mfma32(const u32x4 a, const u32x4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                 0);
+}
+__device__ __forceinline__ u32x2 ld2w(const bf16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ u32x4 cat(const u32x2 a, const u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
+
+template <typename E, int RT>
+struct Stage;
+
+// One chunk of one wave with bf16 I/O (see the chunked form above): returns
+// the wave's 16 columns of y for the chunk's 16 tokens (register r at lane
+// (column, G) is token 4 G + r) and updates S in place. In every MFMA, the A
+// and B operands of lane group G carry the same contraction indices in the
+// same element order, which is all the product needs.
+template <typename St, int RT>
+__device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int G, int c16) {
+  // A^T[s][t] = k_s . q_t over dk: 32 indices per MFMA, 16 for an odd tile
+  v4f At = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ch = 0; ch < RT / 2; ++ch) {
+    const u32x4 ka = *reinterpret_cast<const u32x4*>(&s.k[c16][32 * ch + 8 * G]);
+    const u32x4 qa = *reinterpret_cast<const u32x4*>(&s.q[c16][32 * ch + 8 * G]);
+    At = mfma32(ka, qa, At);
+  }
+  if constexpr (RT % 2 == 1) {
+    const int i = 16 * (RT - 1) + 4 * G;
+    At = mfma16(ld2w(&s.k[c16][i]), ld2w(&s.q[c16][i]), At);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Y = (A o L) V: M[t][4 G + r] in register r is the A operand of token
+  // slots 4 G .. 4 G + 3; v of those tokens for this column from the grouped v
+  const v4f mt = At * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
+  const u32x2 vraw = ld2w(&s.vg[G * St::VGS + (16 * w + c16) * 4]);
+  const Split4 ms = split4(mt);
+  v4f Y = {0.0f, 0.0f, 0.0f, 0.0f};
+  Y = mfma16(ms.hi, vraw, Y);
+  Y = mfma16(ms.mid, vraw, Y);
+  Y = mfma16(ms.lo, vraw, Y);
+  __builtin_amdgcn_sched_barrier(0);
+  // Z = Q S_prev: rows 16 rt + 4 G + r of S are the B operand of index slots
+  // 4 G + r of tile rt; two tiles per 32-index MFMA
+  v4f Z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int pr = 0; pr < RT / 2; ++pr) {
+    const u32x4 qa = cat(ld2w(&s.q[c16][32 * pr + 4 * G]), ld2w(&s.q[c16][32 * pr + 16 + 4 * G]));
+    const Split4 s0 = split4(S[2 * pr]), s1 = split4(S[2 * pr + 1]);
+    Z = mfma32(qa, cat(s0.hi, s1.hi), Z);
+    Z = mfma32(qa, cat(s0.mid, s1.mid), Z);
+    Z = mfma32(qa, cat(s0.lo, s1.lo), Z);
+    __builtin_amdgcn_sched_barrier(0);  // one pair's split terms live at a time
+  }
+  if constexpr (RT % 2 == 1) {
+    const u32x2 qa = ld2w(&s.q[c16][16 * (RT - 1) + 4 * G]);
+    const Split4 sl = split4(S[RT - 1]);
+    Z = mfma16(qa, sl.hi, Z);
+    Z = mfma16(qa, sl.mid, Z);
+    Z = mfma16(qa, sl.lo, Z);
+  }
+  Y += *reinterpret_cast<const v4f*>(&s.P[4 * G]) * Z;
+  // S <- P_15 S + K^T (L[15] o V): the weighted v of token slots 4 G .. 4 G + 3
+  // (the same for every row tile), k of those tokens for row 16 rt + c16
+  const v4f wv = v4f{__builtin_bit_cast(float, vraw.x << 16), __builtin_bit_cast(float, vraw.x & 0xffff0000u),
+                     __builtin_bit_cast(float, vraw.y << 16), __builtin_bit_cast(float, vraw.y & 0xffff0000u)} *
+                 *reinterpret_cast<const v4f*>(&s.L[kT - 1][4 * G]);
+  const Split4 ws = split4(wv);
+  const float p15 = s.P[kT - 1];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const u32x2 kt = ld2w(&s.kg[G * St::KGS + (16 * rt + c16) * 4]);
+    S[rt] *= p15;
+    S[rt] = mfma16(kt, ws.hi, S[rt]);
+    S[rt] = mfma16(kt, ws.mid, S[rt]);
+    S[rt] = mfma16(kt, ws.lo, S[rt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return Y;
+}
+
 template <typename E, int RT>
 struct Stage {
   static constexpr int DKP = 16 * RT;                     // dk padded
@@ -97,6 +221,7 @@ struct Stage {
   E vg[4 * VGS];  // v[t][j] at [t / 4][j][t % 4]
   float L[kT][kLS];
   float P[kT];
+  E y[kT][kCols + 16 / sizeof(E)];  // the chunk's y, stored one chunk later as whole rows
 };
 
 template <typename IoT, typename StT, int RT, bool VEC>
@@ -153,19 +278,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
         const int t = e / (DKP / VEC_E);
         const int i = (e - t * (DKP / VEC_E)) * VEC_E;
         const bool in = e < QV && t0 + t < L && i < dk;
-        const int64_t off = (t0 + t) * dk + i;
-        qr[n] = in ? *reinterpret_cast<const u32x4*>(qg + off) : u32x4{0, 0, 0, 0};
-        kr[n] = in ? *reinterpret_cast<const u32x4*>(kgp + off) : u32x4{0, 0, 0, 0};
+        // a block-uniform base and a small lane offset (no per-lane 64-bit
+        // addresses to keep live across the loop)
+        const int off = t * dk + i;
+        qr[n] = in ? *reinterpret_cast<const u32x4*>(qg + t0 * dk + off) : u32x4{0, 0, 0, 0};
+        kr[n] = in ? *reinterpret_cast<const u32x4*>(kgp + t0 * dk + off) : u32x4{0, 0, 0, 0};
       }
       {
         const int t = tid / (kCols / VEC_E);
         const int j = (tid - t * (kCols / VEC_E)) * VEC_E;
         const bool in = tid < VV && t0 + t < L && jb + j < dv;
-        vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 + t) * dv + jb + j) : u32x4{0, 0, 0, 0};
+        vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 * dv + jb) + static_cast<int>(t * dv + j))
+                : u32x4{0, 0, 0, 0};
       }
     }
     // gamma of token t0 + (tid mod 16), 1 past L
     gam = t0 + (tid & 15) < L ? gg[t0 + (tid & 15)] : 1.0f;
+  };
+
+  // y of the chunk starting at t0, from s.y: 16 rows of 64 columns, whole
+  // 16-byte row segments when rows allow
+  IoT* __restrict__ yg = static_cast<IoT*>(p.y) + b * L * dv;
+  auto store_y = [&](const St& s, int64_t t0) {
+    IoT* yt = yg + t0 * dv + jb;  // block-uniform
+    if constexpr (VEC) {
+      constexpr int RV = kCols / VEC_E;  // vectors per row
+      for (int e = tid; e < kT * RV; e += kThreads) {
+        const int t = e / RV, j = (e - t * RV) * VEC_E;
+        if (t0 + t < L && jb + j < dv)
+          *reinterpret_cast<u32x4*>(yt + static_cast<int64_t>(t) * dv + j) =
+              *reinterpret_cast<const u32x4*>(&s.y[t][j]);
+      }
+    } else {
+      for (int e = tid; e < kT * kCols; e += kThreads) {
+        const int t = e / kCols, j = e - t * kCols;
+        if (t0 + t < L && jb + j < dv) yt[static_cast<int64_t>(t) * dv + j] = s.y[t][j];
+      }
+    }
   };
 
   auto write_stage = [&](St& s, int64_t t0) {
@@ -229,58 +378,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
     write_stage(s, t0);
     __syncthreads();
     if (ch + 1 < nchunks) prefetch(t0 + kT);
+    if (ch > 0) store_y(stage[(ch - 1) & 1], t0 - kT);
     if (!wave_live) continue;
 
-    // A^T[s][t] = k_s . q_t: register r at lane (t, G) is s = 4 G + r
-    v4f A0 = {0.0f, 0.0f, 0.0f, 0.0f}, A1 = A0;
+    v4f Y;
+    if constexpr (sizeof(IoT) == 2) {
+      Y = chunk_bf16<St, RT>(s, S, w, G, c16);
+    } else {
+      // A^T[s][t] = k_s . q_t: register r at lane (t, G) is s = 4 G + r
+      v4f A0 = {0.0f, 0.0f, 0.0f, 0.0f}, A1 = A0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int i = 16 * rt + 4 * G;
-      const v4f ka = ld4(&s.k[c16][i]);
-      const v4f qa = ld4(&s.q[c16][i]);
+      for (int rt = 0; rt < RT; ++rt) {
+        const int i = 16 * rt + 4 * G;
+        const v4f ka = ld4(&s.k[c16][i]);
+        const v4f qa = ld4(&s.q[c16][i]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (rt & 1) A1 = mfma4(ka[g], qa[g], A1);
-        else A0 = mfma4(ka[g], qa[g], A0);
+        for (int g = 0; g < 4; ++g) {
+          if (rt & 1) A1 = mfma4(ka[g], qa[g], A1);
+          else A0 = mfma4(ka[g], qa[g], A0);
+        }
+      }
+      // M[t][s] = A[t][s] L[t][s]: the A operand of M V with slot s = 4 G + g
+      const v4f mt = (A0 + A1) * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
+      const v4f vb = ld4(&s.vg[G * St::VGS + (16 * w + c16) * 4]);  // v[4 G + g][column]
+      Y = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) Y = mfma4(mt[g], vb[g], Y);
+      // Z[t][j] = q_t . S_prev[:, j]
+      asm volatile("" ::: "memory");  // q is read again below rather than held
+      v4f Z0 = {0.0f, 0.0f, 0.0f, 0.0f}, Z1 = Z0;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const v4f qa = ld4(&s.q[c16][16 * rt + 4 * G]);  // read again: fewer live registers
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (rt & 1) Z1 = mfma4(qa[g], S[rt][g], Z1);
+          else Z0 = mfma4(qa[g], S[rt][g], Z0);
+        }
+      }
+      Y += *reinterpret_cast<const v4f*>(&s.P[4 * G]) * (Z0 + Z1);
+      // S <- P_15 S + sum_s (L[15][s] k_s) v_s^T
+      const float p15 = s.P[kT - 1];
+      const v4f l15 = *reinterpret_cast<const v4f*>(&s.L[kT - 1][4 * G]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const v4f kt = ld4(&s.kg[G * St::KGS + (16 * rt + c16) * 4]) * l15;
+        S[rt] *= p15;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) S[rt] = mfma4(kt[g], vb[g], S[rt]);
       }
     }
-    // M[t][s] = A[t][s] L[t][s]: the A operand of M V with slot s = 4 G + g
-    const v4f mt = (A0 + A1) * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
-    const v4f vb = ld4(&s.vg[G * St::VGS + (16 * w + c16) * 4]);  // v[4 G + g][column]
-    v4f Y = {0.0f, 0.0f, 0.0f, 0.0f};
+    // y: register r at lane (column, G) is token 4 G + r; to LDS, stored
+    // with the next chunk (after its barrier)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) Y = mfma4(mt[g], vb[g], Y);
-    // Z[t][j] = q_t . S_prev[:, j]
-    asm volatile("" ::: "memory");  // q is read again below rather than held
-    v4f Z0 = {0.0f, 0.0f, 0.0f, 0.0f}, Z1 = Z0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const v4f qa = ld4(&s.q[c16][16 * rt + 4 * G]);  // read again: fewer live registers
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (rt & 1) Z1 = mfma4(qa[g], S[rt][g], Z1);
-        else Z0 = mfma4(qa[g], S[rt][g], Z0);
-      }
-    }
-    Y += *reinterpret_cast<const v4f*>(&s.P[4 * G]) * (Z0 + Z1);
-    // S <- P_15 S + sum_s (L[15][s] k_s) v_s^T
-    const float p15 = s.P[kT - 1];
-    const v4f l15 = *reinterpret_cast<const v4f*>(&s.L[kT - 1][4 * G]);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const v4f kt = ld4(&s.kg[G * St::KGS + (16 * rt + c16) * 4]) * l15;
-      S[rt] *= p15;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) S[rt] = mfma4(kt[g], vb[g], S[rt]);
-    }
-    // y: register r at lane (column, G) is token 4 G + r
-    if (jc < dv) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t tt = t0 + 4 * G + r;
-        if (tt < L) static_cast<IoT*>(p.y)[(b * L + tt) * dv + jc] = Io<IoT>::from_f32(Y[r]);
-      }
-    }
+    for (int r = 0; r < 4; ++r) s.y[4 * G + r][16 * w + c16] = Io<IoT>::from_f32(Y[r]);
+  }
+  if (nchunks > 0) {
+    __syncthreads();
+    store_y(stage[(nchunks - 1) & 1], (nchunks - 1) * kT);
   }
 
   if (p.final_state && jc < dv) {
@@ -303,7 +458,8 @@ hipError_t launch_rt(const GatedParams& p0, hipStream_t stream) {
   // 16-byte vectors: whole vectors per row and 16-byte aligned bases
   constexpr int VEC_E = 16 / sizeof(IoT);
   const bool vec = p.dk % VEC_E == 0 && p.dv % VEC_E == 0 && reinterpret_cast<uintptr_t>(p.q) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(p.k) % 16 == 0 && reinterpret_cast<uintptr_t>(p.v) % 16 == 0;
+                   reinterpret_cast<uintptr_t>(p.k) % 16 == 0 && reinterpret_cast<uintptr_t>(p.v) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.y) % 16 == 0;
   void* args[] = {&p};
   const void* fn = vec ? reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, true>)
                        : reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, false>);
