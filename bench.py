@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 TRANS_FLOP_EQ = 8.0        # one transcendental issues at 1/4 the FMA rate: 4 FMA slots = 8 flops
 
 
@@ -188,7 +189,9 @@ def gated_work(batch, L, dk, dv, es):
 def measure_gated(ss, stream, reps: int = 20):
     """ss_gated_scan at batch x heads 640, seq 2048, dk 128, dv 64, bf16 I/O,
     fp32 final state (a Mamba-2 2.7B-shaped layer at batch 8: 80 heads of
-    width 64, state 128). Per-launch HIP-event average after a warm-up."""
+    width 64, state 128). Per-launch HIP-event average after a warm-up.
+    Reported against the model's flops (the chunked form, as fp32 work) and
+    against what the bf16 matrix cores execute (split terms included)."""
     import torch
     from selective_state_space_ss_amd.workloads import make_gated_case
     batch, L, dk, dv = GATED_SHAPE
@@ -208,10 +211,21 @@ def measure_gated(ss, stream, reps: int = 20):
     us = e0.elapsed_time(e1) / reps * 1e3
     nbytes, flops = gated_work(batch, L, dk, dv, 2)
     tf = flops / (us * 1e-6) / 1e12
+    # executed on the bf16 matrix cores (bf16 I/O): per 16-token chunk and
+    # 16 value columns, q k^T 16 x 16 x dk, the three split terms of M v
+    # (16 x 16 x 16 each), of q S (16 x 16 x dk each) and of the state update
+    # (dk x 16 x 16 each)
+    chunks = (L + 15) // 16
+    per = 2 * 16 * 16 * dk + 3 * 2 * 16 * 16 * 16 + 3 * 2 * 16 * 16 * dk + 3 * 2 * dk * 16 * 16
+    executed = float(batch * ((dv + 15) // 16) * chunks * per)
+    te = executed / (us * 1e-6) / 1e12
     return {"shape": {"batch_x_heads": batch, "seq": L, "dk": dk, "dv": dv, "io": "bf16", "state": "f32"},
             "us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "mfma_flops": flops,
-            "TFLOP_s": round(tf, 2), "mfma_fp32_frac": round(tf / PEAK_FP32_TFLOPS, 4)}
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "model_flops": flops, "model_TFLOP_s": round(tf, 2),
+            "model_frac_of_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+            "bf16_mfma_flops_executed": executed, "bf16_mfma_TFLOP_s": round(te, 2),
+            "bf16_mfma_frac": round(te / PEAK_BF16_TFLOPS, 4)}
 
 
 ATTN_SHAPE = (1, 1536, 16, 256)   # batch, channels, state_dim, seq
