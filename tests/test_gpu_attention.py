@@ -137,3 +137,15 @@ def test_attention_errors():
     with pytest.raises(ss.SSError) as e:
         ss.ss_effective_attention(dt_view, inp["A"], inp["B"], inp["C"], inp["dt_bias"], out=big)
     assert e.value.code == 5
+
+
+def test_attention_edges():
+    """Zero-size calls are no-ops; one channel of one token is C . B."""
+    print("attention edges", flush=True)
+    inp = to_dev(make_case(1293, 1, 3, 16, 0, "f32", gate=False, h0=False))
+    assert run(inp).shape == (1, 3, 0, 0)
+    inp = make_case(1294, 2, 1, 5, 1, "f32", gate=False, h0=False)
+    M = run(to_dev(inp))
+    torch.cuda.synchronize()
+    ref = (np64(inp["C"])[:, :, 0] * np64(inp["B"])[:, :, 0]).sum(1)
+    assert np.allclose(np64(M)[:, 0, 0, 0], ref, rtol=1e-5, atol=1e-6)

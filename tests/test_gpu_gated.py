@@ -2,8 +2,10 @@
 Gated State Scan" problem page (S_t = gamma_t S_{t-1} + k_t v_t^T,
 y_t = q_t^T S_t), against the fp64 oracle on the same seeded inputs.
 
-Tolerance, from the arithmetic. The kernel computes in fp32 (the page asks
-for fp32 intermediates); every output element is a sum of products whose
+Tolerance, from the arithmetic. The kernel accumulates in fp32 (the page
+asks for fp32 intermediates; with bf16 I/O the products run on the bf16
+matrix cores on exact three-term splits of the fp32 operands, so each product
+is exact and only the fp32 accumulation rounds); every output element is a sum of products whose
 magnitudes add up to what the same scan gives on |q|, |k|, |v|, |s0| (all
 weights gamma are >= 0), here called the absolute sum. An fp32 sum of n
 terms errs by at most n u times its absolute sum (u = 2^-24), typically
@@ -202,3 +204,18 @@ def test_full_size_sampled():
         yr, fr, ya, fa = oracle_run(sl)
         check(y[b:b + 1], yr, ya, torch.bfloat16, f"y[{b}]")
         check(fs[b:b + 1], fr, fa, torch.float32, f"final_state[{b}]")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_gated_edges(io):
+    """A value width that is not a whole vector (element-wise staging), one
+    token, one key row, and the widest key (256) with a single value column."""
+    print(f"gated edges io={io}", flush=True)
+    for seed, (batch, L, dk, dv) in enumerate([(2, 33, 24, 13), (3, 1, 1, 5), (1, 40, 256, 1)]):
+        c = make_gated_case(960 + seed, batch, L, dk, dv, io, s0=True, state_dtype="f32")
+        d = to_dev(c)
+        y, fs = ss.ss_gated_scan(d["q"], d["k"], d["v"], d["gamma"], d["s0"])
+        torch.cuda.synchronize()
+        yr, fr, ya, fa = oracle_run(c)
+        check(y, yr, ya, y.dtype, f"y {batch}x{L}x{dk}x{dv}")
+        check(fs, fr, fa, torch.float32, f"final_state {batch}x{L}x{dk}x{dv}")

@@ -143,3 +143,30 @@ def test_chain_into_the_scan(io):
     xr = oracle.conv1d_silu(np64(c["x_pre"]), np64(c["conv_w"]), np64(c["conv_b"]), reset=c["reset"].numpy())
     dtr = oracle.dt_proj(np64(c["w_dt"]), np64(c["delta"]))
     assert np.allclose(np64(x), xr, rtol=rtol, atol=atol) and np.allclose(np64(dt), dtr, rtol=rtol, atol=atol)
+
+
+def test_producer_edges():
+    """Zero-size calls are no-ops; a rank beyond the streaming form (300 > 8
+    chunks of 32) and a row length that is not a whole vector take the
+    general path; width 8 with a reset on every token reads only the token
+    itself."""
+    print("producer edges", flush=True)
+    c = dev(make_producer_case(1700, 1, 4, 0, 4, 16, "bf16"))
+    assert ss.ss_conv1d_silu(c["x_pre"], c["conv_w"], c["conv_b"]).shape == (1, 4, 0)
+    assert ss.ss_dt_proj(c["w_dt"], c["delta"]).shape == (1, 4, 0)
+    for L, R in ((64, 300), (37, 64)):
+        c = make_producer_case(1701 + L, 2, 40, L, 4, R, "bf16")
+        d = dev(c)
+        dt = ss.ss_dt_proj(d["w_dt"], d["delta"], d["dt_bias"], apply_softplus=True)
+        torch.cuda.synchronize()
+        w, delta = np64(c["w_dt"]), np64(c["delta"])
+        ref = oracle.dt_proj(w, delta, dt_bias=np64(c["dt_bias"]), apply_softplus=True)
+        scale = np.stack([np.abs(w) @ np.abs(delta[b]).T for b in range(2)])
+        check(dt, ref, scale, R, torch.bfloat16, f"dt L={L} R={R}")
+    c = make_producer_case(1703, 1, 3, 40, 8, 16, "f32")
+    c["reset"] = torch.ones(1, 40, dtype=torch.uint8)
+    d = dev(c)
+    x = ss.ss_conv1d_silu(d["x_pre"], d["conv_w"], d["conv_b"], d["reset"])
+    torch.cuda.synchronize()
+    pre = np64(c["conv_w"])[:, -1][None, :, None] * np64(c["x_pre"]) + np64(c["conv_b"])[None, :, None]
+    check(x, pre / (1.0 + np.exp(-pre)), np.abs(pre) + 1.0, 1, torch.float32, "x, reset on every token")
