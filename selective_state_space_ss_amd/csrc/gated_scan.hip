@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
         const int t = tid / (kCols / VEC_E);
         const int j = (tid - t * (kCols / VEC_E)) * VEC_E;
         const bool in = tid < VV && t0 + t < L && jb + j < dv;
-        vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 * dv + jb) + static_cast<int>(t * dv + j))
+        vr = in ? *reinterpret_cast<const u32x4*>(vgp + (t0 * dv + jb) + (static_cast<int64_t>(t) * dv + j))
                 : u32x4{0, 0, 0, 0};
       }
     }
