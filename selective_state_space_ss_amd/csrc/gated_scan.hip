@@ -438,13 +438,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
     store_y(stage[(nchunks - 1) & 1], (nchunks - 1) * kT);
   }
 
-  if (p.final_state && jc < dv) {
+  // The lane's column and lane group go through opaque copies here, so that
+  // the compiler does not keep the prologue's per-element s0 offsets (the
+  // same expressions) live across the whole chunk loop.
+  int c16e = c16, Ge = G;
+  asm volatile("" : "+v"(c16e), "+v"(Ge));
+  const int64_t jce = jw + c16e;
+  if (p.final_state && jce < dv) {
+    StT* fs = static_cast<StT*>(p.final_state) + b * dk * dv + jce;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * rt + 4 * G + r;
-        if (i < dk) static_cast<StT*>(p.final_state)[(b * dk + i) * dv + jc] = Io<StT>::from_f32(S[rt][r]);
+        const int i = 16 * rt + 4 * Ge + r;
+        if (i < dk) fs[static_cast<int64_t>(i) * dv] = Io<StT>::from_f32(S[rt][r]);
       }
   }
 }
