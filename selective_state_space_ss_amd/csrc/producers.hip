@@ -6,9 +6,9 @@
 // conv1d_silu: x[b, c, t] = silu(conv_b[c] + sum_k conv_w[c, k] x_pre[b, c, t - (W-1) + k]),
 // a depthwise causal convolution of width W <= 8; a tap before position 0 or
 // before the current document's first token (reset[b, s] != 0) reads 0.
-// Bound by HBM (one read of x_pre, one write of x). A thread makes 8
-// consecutive tokens of one row from 16 elements (its 8 and the 8 before
-// them, for the taps), with 16-byte loads and stores where rows allow.
+// Bound by HBM (one read of x_pre, one write of x). A wave makes a segment of
+// 2048 tokens of one row, each load and store instruction covering 64
+// consecutive 8-token runs (see the kernel).
 //
 // dt_proj: dt[b, c, t] = sum_k w_dt[c, k] delta[b, t, k] (optionally
 // softplus(dt + dt_bias[c])), a GEMM of channels x tokens over the rank k on
@@ -30,95 +30,114 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------ conv1d + SiLU
-constexpr int kConvTok = 8;        // tokens per thread
+constexpr int kConvRun = 8;        // tokens per run (one 16-byte bf16 vector)
+constexpr int kConvRuns = 4;       // runs per thread
+constexpr int kConvSeg = 64 * kConvRuns * kConvRun;  // tokens per wave: a segment of a row
 constexpr int kConvThreads = 256;
-constexpr int kMaxWidth = 8;
 
-template <typename IoT, bool VEC>
+// Wave layout: a wave owns a segment of kConvSeg tokens of one row; run n
+// of lane l is the 8 tokens at seg + (64 n + l) * 8, so every load and store
+// instruction of the wave covers 64 consecutive runs (1 KiB of bf16). The 8
+// tokens before a run (for the taps) are loaded the same way, from cache.
+// MAXW: the width bound the tap loop is unrolled for (4 or 8); RESET: a
+// reset mask is given (else the taps need no document bookkeeping).
+template <typename IoT, bool VEC, int MAXW, bool RESET>
 __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(const ConvParams p) {
+  constexpr int E = 16 / sizeof(IoT);   // elements per 16-byte vector
+  constexpr int RV = kConvRun / E;      // vectors per run
   const int64_t L = p.L;
-  const int64_t chunks = (L + kConvTok - 1) / kConvTok;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x;
-  if (g >= p.rows * chunks) return;
-  const int64_t row = g / chunks;               // b * channels + c
-  const int64_t t0 = (g - row * chunks) * kConvTok;
+  const int64_t segs = (L + kConvSeg - 1) / kConvSeg;
+  const int64_t wv = (static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x) >> 6;
+  if (wv >= p.rows * segs) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = wv / segs;               // b * channels + c
+  const int64_t seg0 = (wv - row * segs) * kConvSeg;
   const int64_t b = row / p.channels, c = row - b * p.channels;
   const IoT* __restrict__ xp = static_cast<const IoT*>(p.x_pre) + row * L;
+  IoT* __restrict__ xo = static_cast<IoT*>(p.x) + row * L;
   const int W = p.W;
 
-  // v[u] = x_pre at t0 - 8 + u, u in [0, 16); positions outside [0, L) are 0
-  float v[2 * kConvTok];
-  if constexpr (VEC) {
-    // rows are whole 16-byte vectors and t0 is a multiple of 8
-    if constexpr (sizeof(IoT) == 2) {
-      u32x4 cur = *reinterpret_cast<const u32x4*>(xp + t0);
-      u32x4 prev = t0 > 0 ? *reinterpret_cast<const u32x4*>(xp + t0 - kConvTok) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pw = prev[e], cw = cur[e];
-        v[2 * e] = __builtin_bit_cast(float, pw << 16);
-        v[2 * e + 1] = __builtin_bit_cast(float, pw & 0xffff0000u);
-        v[kConvTok + 2 * e] = __builtin_bit_cast(float, cw << 16);
-        v[kConvTok + 2 * e + 1] = __builtin_bit_cast(float, cw & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const v4f cur = *reinterpret_cast<const v4f*>(xp + t0 + 4 * h);
-        const v4f prev = t0 > 0 ? *reinterpret_cast<const v4f*>(xp + t0 - kConvTok + 4 * h) : v4f{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[4 * h + e] = prev[e];
-          v[kConvTok + 4 * h + e] = cur[e];
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 2 * kConvTok; ++u) {
-      const int64_t s = t0 - kConvTok + u;
-      v[u] = (s >= 0 && s < L) ? Io<IoT>::to_f32(xp[s]) : 0.0f;
-    }
-  }
-  // reset flags of the same 16 positions (1 = a document starts there)
-  bool start[2 * kConvTok];
-#pragma unroll
-  for (int u = 0; u < 2 * kConvTok; ++u) {
-    const int64_t s = t0 - kConvTok + u;
-    start[u] = p.reset && s >= 0 && s < L && p.reset[b * L + s] != 0;
-  }
   // wr[m]: the weight of the tap m tokens back (conv_w[c, W - 1 - m]), 0 past W
-  float wr[kMaxWidth];
+  float wr[MAXW];
 #pragma unroll
-  for (int m = 0; m < kMaxWidth; ++m) wr[m] = m < W ? p.conv_w[c * W + (W - 1 - m)] : 0.0f;
+  for (int m = 0; m < MAXW; ++m) wr[m] = m < W ? p.conv_w[c * W + (W - 1 - m)] : 0.0f;
   const float bias = p.conv_b ? p.conv_b[c] : 0.0f;
 
-  float out[kConvTok];
-#pragma unroll
-  for (int u = 0; u < kConvTok; ++u) {
-    // token t0 + u is v[8 + u]; the tap m tokens back reads v[8 + u - m],
-    // until a document start has been passed (weights past W are 0)
-    float acc = bias;
-    bool open = true;
-#pragma unroll
-    for (int m = 0; m < kMaxWidth; ++m) {
-      acc = open ? __builtin_fmaf(wr[m], v[kConvTok + u - m], acc) : acc;
-      open = open && !start[kConvTok + u - m];
-    }
-    out[u] = silu_f32(acc);
-  }
-  IoT* __restrict__ xo = static_cast<IoT*>(p.x) + row * L;
+  // every load of the thread first: run n and the 8 tokens before it
+  u32x4 cur[kConvRuns][RV], prv[kConvRuns][RV];
+  float v[kConvRuns][2 * kConvRun];  // [0, 8): before the run, [8, 16): the run
   if constexpr (VEC) {
-    if constexpr (sizeof(IoT) == 2) {
-      store_vec16(reinterpret_cast<bf16_t*>(xo + t0), out);
-    } else {
-      store_vec16(reinterpret_cast<float*>(xo + t0), out);
-      store_vec16(reinterpret_cast<float*>(xo + t0 + 4), out + 4);
+    // rows are whole 8-token runs (L % 8 == 0, 16-byte aligned): every run
+    // is entirely inside or entirely past the row
+#pragma unroll
+    for (int n = 0; n < kConvRuns; ++n) {
+      const int64_t t0 = seg0 + (64 * n + lane) * kConvRun;
+#pragma unroll
+      for (int h = 0; h < RV; ++h) {
+        cur[n][h] = t0 < L ? *reinterpret_cast<const u32x4*>(xp + t0 + h * E) : u32x4{0, 0, 0, 0};
+        prv[n][h] = (t0 > 0 && t0 < L) ? *reinterpret_cast<const u32x4*>(xp + t0 - kConvRun + h * E)
+                                       : u32x4{0, 0, 0, 0};
+      }
     }
+#pragma unroll
+    for (int n = 0; n < kConvRuns; ++n)
+#pragma unroll
+      for (int h = 0; h < RV; ++h) {
+        unpack_vec16<IoT>(uint4{prv[n][h][0], prv[n][h][1], prv[n][h][2], prv[n][h][3]}, &v[n][h * E]);
+        unpack_vec16<IoT>(uint4{cur[n][h][0], cur[n][h][1], cur[n][h][2], cur[n][h][3]}, &v[n][kConvRun + h * E]);
+      }
   } else {
 #pragma unroll
-    for (int u = 0; u < kConvTok; ++u)
-      if (t0 + u < L) xo[t0 + u] = Io<IoT>::from_f32(out[u]);
+    for (int n = 0; n < kConvRuns; ++n) {
+      const int64_t t0 = seg0 + (64 * n + lane) * kConvRun;
+#pragma unroll
+      for (int u = 0; u < 2 * kConvRun; ++u) {
+        const int64_t s = t0 - kConvRun + u;
+        v[n][u] = (s >= 0 && s < L) ? Io<IoT>::to_f32(xp[s]) : 0.0f;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int n = 0; n < kConvRuns; ++n) {
+    const int64_t t0 = seg0 + (64 * n + lane) * kConvRun;
+    if (t0 >= L) continue;
+    // reset flags of the run and the 8 tokens before it (bit u: position t0 - 8 + u)
+    uint32_t start = 0;
+    if constexpr (RESET) {
+#pragma unroll
+      for (int u = 0; u < 2 * kConvRun; ++u) {
+        const int64_t s = t0 - kConvRun + u;
+        if (s >= 0 && s < L && p.reset[b * L + s] != 0) start |= 1u << u;
+      }
+    }
+    float out[kConvRun];
+#pragma unroll
+    for (int u = 0; u < kConvRun; ++u) {
+      // token t0 + u is v[n][8 + u]; the tap m tokens back reads v[n][8 + u - m],
+      // until a document start has been passed (weights past W are 0)
+      float acc = bias;
+      if constexpr (RESET) {
+        bool open = true;
+#pragma unroll
+        for (int m = 0; m < MAXW; ++m) {
+          acc = open ? __builtin_fmaf(wr[m], v[n][kConvRun + u - m], acc) : acc;
+          open = open && !((start >> (kConvRun + u - m)) & 1u);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MAXW; ++m) acc = __builtin_fmaf(wr[m], v[n][kConvRun + u - m], acc);
+      }
+      out[u] = silu_f32(acc);
+    }
+    if constexpr (VEC) {
+#pragma unroll
+      for (int h = 0; h < RV; ++h) store_vec16(reinterpret_cast<IoT*>(xo + t0 + h * E), out + h * E);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kConvRun; ++u)
+        if (t0 + u < L) xo[t0 + u] = Io<IoT>::from_f32(out[u]);
+    }
   }
 }
 
@@ -347,15 +366,25 @@ hipError_t launch_stream(const ProjParams& p, hipStream_t stream) {
 
 template <typename IoT>
 hipError_t launch_conv_io(const ConvParams& p, hipStream_t stream) {
-  const int64_t chunks = (p.L + kConvTok - 1) / kConvTok;
-  const int64_t threads = p.rows * chunks;
-  const int64_t blocks = (threads + kConvThreads - 1) / kConvThreads;
+  const int64_t waves = p.rows * ((p.L + kConvSeg - 1) / kConvSeg);
+  const int64_t blocks = (waves * 64 + kConvThreads - 1) / kConvThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const bool vec = p.L % kConvTok == 0 && reinterpret_cast<uintptr_t>(p.x_pre) % 16 == 0 &&
+  const bool vec = p.L % kConvRun == 0 && reinterpret_cast<uintptr_t>(p.x_pre) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(p.x) % 16 == 0;
   void* args[] = {const_cast<ConvParams*>(&p)};
-  const void* fn = vec ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true>)
-                       : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false>);
+  const bool reset = p.reset != nullptr, narrow = p.W <= 4;
+  const void* fn;
+  if (vec) {
+    if (narrow) fn = reset ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true, 4, true>)
+                           : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true, 4, false>);
+    else fn = reset ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true, 8, true>)
+                    : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, true, 8, false>);
+  } else {
+    if (narrow) fn = reset ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 4, true>)
+                           : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 4, false>);
+    else fn = reset ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 8, true>)
+                    : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 8, false>);
+  }
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kConvThreads), args, 0, stream);
 }
 
@@ -404,7 +433,7 @@ hipError_t launch_dt_proj(const ProjParams& p, bool io_bf16, hipStream_t stream)
 }
 
 bool producer_grids_ok(int64_t batch, int64_t channels, int64_t L) {
-  const int64_t conv_blocks = (batch * channels * ((L + kConvTok - 1) / kConvTok) + kConvThreads - 1) / kConvThreads;
+  const int64_t conv_blocks = (batch * channels * ((L + kConvSeg - 1) / kConvSeg) * 64 + kConvThreads - 1) / kConvThreads;
   const int64_t proj_blocks = batch * ((channels + kProjC - 1) / kProjC) * ((L + kProjT - 1) / kProjT);
   return conv_blocks <= 0x7fffffff && proj_blocks <= 0x7fffffff;
 }
