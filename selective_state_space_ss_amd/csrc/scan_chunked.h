@@ -83,6 +83,9 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
   __shared__ float sC[NG][kRowLanes][KP];
   __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
   __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
+  // kAllStates: one coordinate's states of the chunk per row, each lane's K
+  // tokens padded to KP, re-read in token order for coalesced stores
+  __shared__ __align__(16) float sSt[STATES == kAllStates ? S::kChan : 1][STATES == kAllStates ? kRowLanes * KP : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -269,22 +272,35 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
             h4[i] = h;
             if constexpr (STATES == kOneState) hsel = j + i == jsel ? h : hsel;
           }
-          if constexpr (STATES == kAllStates) {
-            // states [batch, channels, N, L]: the 16 lanes of a row store a
-            // contiguous run of the row's coordinate n
-            if (n < N && row_ok) {
-              float* dst = p.states + ((b * p.channels + c) * N + n) * L + tb + j;
-              if (full && p.states_vec)
-                *reinterpret_cast<float4*>(dst) = make_float4(h4[0], h4[1], h4[2], h4[3]);
-              else
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (tb + j + i < L) dst[i] = h4[i];
-            }
-          }
+          if constexpr (STATES == kAllStates)
+            *reinterpret_cast<float4*>(&sSt[wave * kRowsPerWave + row][tl * KP + j]) =
+                make_float4(h4[0], h4[1], h4[2], h4[3]);
         }
         if constexpr (STATES == kOneState) {
           if (jsel >= 0 && n < N && row_ok) p.states[(b * p.channels + c) * N + n] = hsel;
+        }
+        if constexpr (STATES == kAllStates) {
+          // states [batch, channels, N, L]: the row's 16 K tokens of
+          // coordinate n, read back in token order from this row's own LDS
+          // slot (written by this wave just above; a wave's LDS accesses
+          // complete in order), so that store q of the 16 lanes covers 64
+          // consecutive tokens
+          if (n < N && row_ok) {
+            float* dst = p.states + ((b * p.channels + c) * N + n) * L + t0;
+#pragma unroll
+            for (int q = 0; q < K / 4; ++q) {
+              const int tok = 64 * q + 4 * tl;  // within the chunk
+              const float4 v4 = *reinterpret_cast<const float4*>(&sSt[wave * kRowsPerWave + row][(tok / K) * KP + tok % K]);
+              if (full && p.states_vec) {
+                *reinterpret_cast<float4*>(dst + tok) = v4;
+              } else {
+                const float hv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (t0 + tok + i < L) dst[tok + i] = hv[i];
+              }
+            }
+          }
         }
       }
     };
@@ -345,7 +361,9 @@ hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   const bool gate = p.z != nullptr, reset = p.reset != nullptr;
   // 8-wave blocks when 4 waves fit per SIMD (two blocks per CU), else 4-wave
   // blocks (three per CU at 3 waves per SIMD)
-  constexpr int W = min_waves_per_simd<IoT, K, false>() == 4 ? 8 : 4;
+  // (the every-token states variant stages a 20 KB tile per 16 channels:
+  // 4-wave blocks keep three blocks per CU)
+  constexpr int W = (min_waves_per_simd<IoT, K, false>() == 4 && STATES != kAllStates) ? 8 : 4;
   constexpr int WR = 4;
   if (gate && reset) return launch_t<IoT, K, WR, NMAX, true, true, STATES>(p, stream);
   if (gate) return launch_t<IoT, K, W, NMAX, true, false, STATES>(p, stream);
