@@ -136,6 +136,28 @@ def recorded_traffic():
     return t["traffic_bytes_per_scan"]
 
 
+EXTRA_WARM_S = 0.3   # each extra kernel runs this long before it is timed
+
+
+def time_launches(f, stream, reps: int) -> float:
+    """Average microseconds per call of f (HIP events on `stream`), after
+    EXTRA_WARM_S seconds of untimed calls (clocks and caches settle)."""
+    import torch
+    t0 = time.time()
+    while True:
+        f()
+        torch.cuda.synchronize()
+        if time.time() - t0 >= EXTRA_WARM_S:
+            break
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
 def measure_states(ss, P, w, scan_bytes: int, stream, reps: int = 20):
     """ss_scan_fwd_states at the prompt workload's shape, outside the timed
     step: every token's state ([batch, channels, N, seq] fp32, 4 N bytes per
@@ -154,16 +176,7 @@ def measure_states(ss, P, w, scan_bytes: int, stream, reps: int = 20):
         f = lambda: ss.ss_scan_fwd_states(P["x"], P["dt"], P["A"], P["B"], P["C"], D=P["D"], z=P["z"],
                                           dt_bias=P["dt_bias"], h0=P["h0"], time_step=ts, y=y, h_last=h,
                                           states=states)
-        for _ in range(3):
-            f()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = time_launches(f, stream, reps)
         nbytes = scan_bytes + extra
         res[label] = {"us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
                       "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -199,16 +212,7 @@ def measure_gated(ss, stream, reps: int = 20):
     y = torch.empty(batch, L, dv, dtype=torch.bfloat16, device="cuda")
     fs = torch.empty(batch, dk, dv, dtype=torch.float32, device="cuda")
     f = lambda: ss.ss_gated_scan(c["q"], c["k"], c["v"], c["gamma"], y=y, final_state=fs)
-    for _ in range(5):
-        f()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        f()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps * 1e3
+    us = time_launches(f, stream, reps)
     nbytes, flops = gated_work(batch, L, dk, dv, 2)
     tf = flops / (us * 1e-6) / 1e12
     # executed on the bf16 matrix cores (bf16 I/O): per 16-token chunk and
@@ -244,16 +248,7 @@ def measure_attention(ss, stream, reps: int = 20):
            for k, v in make_case(1020, batch, channels, N, L, "bf16", gate=False, h0=False).items()}
     out = torch.empty(batch, channels, L, L, dtype=torch.float32, device="cuda")
     f = lambda: ss.ss_effective_attention(inp["dt"], inp["A"], inp["B"], inp["C"], inp["dt_bias"], out=out)
-    for _ in range(5):
-        f()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        f()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps * 1e3
+    us = time_launches(f, stream, reps)
     nbytes = batch * channels * L * L * 4 + batch * channels * L * 2 + 2 * batch * N * L * 2 + channels * (N + 1) * 4
     return {"shape": {"batch": batch, "channels": channels, "state_dim": N, "seq": L, "io": "bf16", "out": "f32"},
             "us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
@@ -283,16 +278,7 @@ def measure_producers(ss, stream, reps: int = 20):
     }
     res = {"shape": {"batch": batch, "channels": channels, "seq": L, "width": W, "rank": R, "io": "bf16"}}
     for name, (f, nbytes, flops) in calls.items():
-        for _ in range(5):
-            f()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = time_launches(f, stream, reps)
         r = {"us": round(us, 2), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
              "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         if flops:
