@@ -209,13 +209,22 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     // 3. per-token step size, dt*x, skip term
     float dtv[K], dtx[K], yv[K], mj[RESET ? K : 1];
     float sdt = 0.0f, mlane = 0.0f;
+    // (uniform branches, so that whole chunks run neither a select per
+    // token for the softplus switch nor the bounds mask)
+    if (p.dt_softplus) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dtv[j] = softplus_f32(dv[j] + bias);
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dtv[j] = dv[j] + bias;
+    }
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) dtv[j] = tb + j < L ? dtv[j] : 0.0f;  // past the end: a = 1, b = 0 (identity)
+    }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const bool in = full || (tb + j < L);
-      const float v = dv[j] + bias;
-      float d = p.dt_softplus ? softplus_f32(v) : v;
-      d = in ? d : 0.0f;  // tokens past the end: a = 1, b = 0 (identity)
-      dtv[j] = d;
+      const float d = dtv[j];
       dtx[j] = d * xv[j];
       yv[j] = Dc * xv[j];
       sdt += d;
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
         for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
         row16_inclusive_scan(Al, Bl);                            // Bl: state after this lane's tokens
         float h = dpp_or<kDppRowShr1>(carry, Bl);                // state before them
-        sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(0.0f, Bl);  // state after the chunk
+        sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(Bl, Bl);    // state after the chunk (in place)
         float hsel = 0.0f;  // kOneState: the state after the selected token
 #pragma unroll
         for (int j = 0; j < K; j += 4) {
