@@ -17,10 +17,14 @@
 // token-major [batch, L, R]), so each lane loads its operand slice with one
 // 16-byte load per 32 (bf16) or 16 (fp32) values of k, straight from L2
 // (w_dt and delta are small next to the dt it writes). Bound by writing dt.
-// Ranks of up to 8 chunks with whole 16-byte rows take the streaming form
-// below; other shapes a plain tile-per-block form.
+// Ranks of up to 8 chunks with whole 16-byte rows take the tiled form below
+// (a grid of resident blocks over equal runs of work units); other shapes a
+// plain tile-per-block form.
 #include "ss_device.h"
 #include "ss_launch.h"
+
+#include <atomic>
+#include <cstdlib>
 
 namespace ss {
 namespace {
@@ -227,141 +231,206 @@ __global__ __launch_bounds__(kProjThreads) void dt_proj_kernel(const ProjParams 
   }
 }
 
-// Streaming form for ranks up to 8 chunks (R <= 256 bf16, 128 fp32) with
-// whole 16-byte rows: a block owns 64 channels of one batch row, keeps their
-// w_dt operand slices in registers, and walks the sequence in 64-token
-// tiles. Each tile of delta ([token][k], k contiguous) is loaded with 16-byte
-// loads one tile ahead into registers, written to one of two LDS buffers and
-// read back as MFMA B operands; the 64 x 64 output tile goes through LDS so
-// that every row of 64 tokens is written with whole 16-byte stores.
-constexpr int kStreamT = 64;
+// Tiled form for ranks up to 8 chunks (R <= 256 bf16, 128 fp32) with whole
+// 16-byte rows. The work is cut into units of (batch row, 256 channels, 64
+// tokens), and a grid of as many blocks as the device keeps resident takes
+// contiguous, equal runs of units (channel groups outer, tokens inner), so
+// that no partial last round of blocks is left. A block is 8 waves; wave w
+// owns 32 channels of the group and keeps their w_dt slices in registers,
+// reloaded only where its run crosses into the next (batch row, group). The
+// 64-token tile of delta of a unit ([token][k], k contiguous) is loaded one
+// unit ahead into registers and staged in one of two LDS buffers, shared by
+// the 8 waves (one barrier per unit). The product is formed transposed
+// (delta as the A operand, w_dt as the B operand), so that a lane's four
+// accumulator registers are four consecutive tokens of one channel: they
+// leave as one 8-byte (bf16) or 16-byte (fp32) LDS write into the wave's own
+// 32 x 64 output tile, which is read back in rows and written with 16-byte
+// stores, 128 (bf16) or 256 (fp32) contiguous bytes per channel.
+constexpr int kProjWaves = 8;
+constexpr int kProjWaveC = 32;                     // channels per wave (two MFMA column tiles)
+constexpr int kProjGroupC = kProjWaves * kProjWaveC;  // channels per unit
+constexpr int kProjStepT = 64;                     // tokens per unit (four MFMA row tiles)
 
 template <typename IoT, int KCH>
-struct ProjStage {
+struct ProjTileLds {
   static constexpr int E = 16 / sizeof(IoT);
-  static constexpr int KP = KCH * 4 * E + E;   // k per staged row, padded by one vector
-  IoT d[2][kStreamT][KP];
-  IoT o[kProjC][kStreamT + E];
-  float bias[kProjC];
+  static constexpr int DP = KCH * 4 * E + E;       // delta row pitch (elements), padded by one vector
+  static constexpr int OP = kProjStepT + E;        // output row pitch
+  IoT d[2][kProjStepT][DP];
+  IoT o[kProjWaves][kProjWaveC][OP];
 };
 
-template <typename IoT, int KCH, bool APPLY>
-__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(KCH <= 5 ? 3 : 1))) void
-dt_proj_stream_kernel(const ProjParams p) {
-  using St = ProjStage<IoT, KCH>;
-  constexpr int E = St::E;
-  constexpr int KC = 4 * E;                      // k per MFMA chunk
-  constexpr int RV = KCH * 4;                    // 16-byte vectors per staged row
-  constexpr int TV = kStreamT * RV;              // vectors per tile
-  constexpr int NPF = (TV + kProjThreads - 1) / kProjThreads;
-  __shared__ __align__(16) St st;
+template <typename IoT, int KCH>
+constexpr int proj_blocks_per_cu() {
+  // two 8-wave blocks need <= 128 registers (KCH <= 5) and <= 80 KB of LDS each
+  return (KCH <= 5 && sizeof(ProjTileLds<IoT, KCH>) <= 80 * 1024) ? 2 : 1;
+}
 
-  // Wave w computes all 64 channels of the block against tokens
-  // [16 w, 16 w + 16) of each tile: every B operand read from LDS feeds the
-  // four channel tiles' MFMAs, whose A operands stay in registers.
+template <typename IoT, int KCH, bool APPLY>
+__global__ __launch_bounds__(64 * kProjWaves) __attribute__((amdgpu_waves_per_eu(2 * proj_blocks_per_cu<IoT, KCH>())))
+void dt_proj_tile_kernel(const ProjParams p) {
+  using Lds = ProjTileLds<IoT, KCH>;
+  constexpr int E = Lds::E;
+  constexpr int KC = 4 * E;                        // k per MFMA chunk
+  constexpr int RV = KCH * 4;                      // 16-byte vectors per staged delta row
+  constexpr int kThreads = 64 * kProjWaves;
+  constexpr int TV = kProjStepT * RV;              // vectors per delta tile
+  constexpr int NPF = (TV + kThreads - 1) / kThreads;
+  constexpr int OV = kProjStepT / E;               // 16-byte vectors per output row
+  __shared__ __align__(16) Lds st;
+
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, r16 = l & 15;
   const int64_t L = p.L, C = p.channels, R = p.R;
-  const int64_t cblocks = (C + kProjC - 1) / kProjC;
-  const int64_t b = blockIdx.x / cblocks;
-  const int64_t cbase = (blockIdx.x - b * cblocks) * kProjC;
-  const IoT* __restrict__ Dg = static_cast<const IoT*>(p.delta) + b * L * R;
-  IoT* __restrict__ out = static_cast<IoT*>(p.dt) + b * C * L;
+  const int64_t nsteps = (L + kProjStepT - 1) / kProjStepT;
+  const int64_t groups = (C + kProjGroupC - 1) / kProjGroupC;
+  const int64_t units = p.batch * groups * nsteps;
+  const int64_t u0 = (int64_t)blockIdx.x * units / gridDim.x;
+  const int64_t u1 = ((int64_t)blockIdx.x + 1) * units / gridDim.x;
+  if (u0 >= u1) return;  // the whole block
+  const IoT* __restrict__ Dall = static_cast<const IoT*>(p.delta);
+  IoT* __restrict__ Oall = static_cast<IoT*>(p.dt);
 
-  // A operands of channel tile m: w_dt[cbase + 16 m + r16][kc * KC + E * G .. + E - 1]
-  u32x4 a[4][KCH];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int64_t c = cbase + 16 * m + r16;
-    const bool c_ok = c < C;
-    const IoT* wrow = static_cast<const IoT*>(p.w_dt) + (c_ok ? c * R : 0);
-#pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) a[m][kc] = load_k16<IoT, true>(wrow, kc * KC + E * G, R, c_ok);
-  }
-
-  if (APPLY && tid < kProjC) st.bias[tid] = (p.dt_bias && cbase + tid < C) ? p.dt_bias[cbase + tid] : 0.0f;
-
+  // block-cooperative delta tile of unit u, through registers
   u32x4 pf[NPF];
-  auto prefetch = [&](int64_t t0) {
+  auto fetch = [&](int64_t u) {
+    const int64_t bg = u / nsteps, b = bg / groups;
+    const int64_t t0 = (u - bg * nsteps) * kProjStepT;
+    const IoT* D = Dall + b * L * R;
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
-      const int e = tid + n * kProjThreads;
+      const int e = tid + n * kThreads;
       const int t = e / RV, kv = (e - t * RV) * E;
       const bool in = e < TV && t0 + t < L && kv < R;
-      pf[n] = in ? *reinterpret_cast<const u32x4*>(Dg + (t0 + t) * R + kv) : u32x4{0, 0, 0, 0};
+      pf[n] = in ? *reinterpret_cast<const u32x4*>(D + (t0 + t) * R + kv) : u32x4{0, 0, 0, 0};
     }
   };
-  const int64_t ntiles = (L + kStreamT - 1) / kStreamT;
-  if (ntiles > 0) prefetch(0);
-  for (int64_t it = 0; it < ntiles; ++it) {
-    const int64_t t0 = it * kStreamT;
-    const int buf = static_cast<int>(it & 1);
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
-      const int e = tid + n * kProjThreads;
+      const int e = tid + n * kThreads;
       if (e < TV) {
         const int t = e / RV, kv = (e - t * RV) * E;
         *reinterpret_cast<u32x4*>(&st.d[buf][t][kv]) = pf[n];
       }
     }
+  };
+
+  fetch(u0);
+  stash(0);
+  if (u0 + 1 < u1) fetch(u0 + 1);
+
+  u32x4 wf[2][KCH];
+  float bias[2] = {0.0f, 0.0f};
+  int64_t wbg = -1;  // (batch row, group) whose w_dt slices are in wf
+  for (int64_t u = u0; u < u1; ++u) {
+    const int buf = static_cast<int>((u - u0) & 1);
+    // unit u's tile is visible, and every wave is done with the other buffer
     __syncthreads();
-    if (it + 1 < ntiles) prefetch(t0 + kStreamT);
-    v4f acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (u + 1 < u1) {
+      stash(buf ^ 1);
+      if (u + 2 < u1) fetch(u + 2);
+    }
+    const int64_t bg = u / nsteps, b = bg / groups, g = bg - b * groups;
+    const int64_t t0 = (u - bg * nsteps) * kProjStepT;
+    const int64_t c0 = g * kProjGroupC + w * kProjWaveC;  // this wave's 32 channels
+    if (bg != wbg) {
+      // B operands of column tile m: lane (r16, G) holds w_dt[c0 + 16 m + r16][kc KC + E G ..]
 #pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) {
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * w + r16][kc * KC + E * G]);
+      for (int m = 0; m < 2; ++m) {
+        const int64_t c = c0 + 16 * m + r16;
+        const bool c_ok = c < C;
+        const IoT* wrow = static_cast<const IoT*>(p.w_dt) + (c_ok ? c * R : 0);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if constexpr (sizeof(IoT) == 2) {
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m][kc]),
-                                                           __builtin_bit_cast(bf16x8, bv), acc[m], 0, 0, 0);
-        } else {
+        for (int kc = 0; kc < KCH; ++kc) wf[m][kc] = load_k16<IoT, true>(wrow, kc * KC + E * G, R, c_ok);
+        bias[m] = (APPLY && p.dt_bias && c_ok) ? p.dt_bias[c] : 0.0f;
+      }
+      wbg = bg;
+    }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t ag = a[m][kc][g], bg = bv[g];
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag),
-                                                           __builtin_bit_cast(float, bg), acc[m], 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      // A operands: lane (r16, G) holds delta[t0 + 16 q + r16][kc KC + E G ..]
+      u32x4 af[KCH];
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) af[kc] = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * q + r16][kc * KC + E * G]);
+      v4f acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if constexpr (sizeof(IoT) == 2) {
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[kc]),
+                                                             __builtin_bit_cast(bf16x8, wf[m][kc]), acc[m], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+              const uint32_t ag = af[kc][gg], bgv = wf[m][kc][gg];
+              acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ag),
+                                                             __builtin_bit_cast(float, bgv), acc[m], 0, 0, 0);
+            }
           }
         }
       }
-    }
-    // D: register r at lane (r16, G) of channel tile m is channel 16 m + 4 G + r,
-    // token 16 w + r16 of the tile
+      // D^T: register r at lane (r16, G) of column tile m is token t0 + 16 q +
+      // 4 G + r of channel c0 + 16 m + r16
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      v4f bm = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (APPLY) bm = *reinterpret_cast<const v4f*>(&st.bias[16 * m + 4 * G]);  // staged before
+      for (int m = 0; m < 2; ++m) {
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[m][r];
-        if constexpr (APPLY) v = softplus_f32(v + bm[r]);
-        st.o[16 * m + 4 * G + r][16 * w + r16] = Io<IoT>::from_f32(v);
-      }
-    }
-    __syncthreads();
-    // rows of 64 tokens, E per 16-byte store
-    constexpr int OV = kStreamT / E;               // vectors per output row
-    for (int e = tid; e < kProjC * OV; e += kProjThreads) {
-      const int cl = e / OV, tv = (e - cl * OV) * E;
-      const int64_t c = cbase + cl, t = t0 + tv;
-      if (c < C && t < L) {
-        if (t + E <= L) {
-          *reinterpret_cast<u32x4*>(out + c * L + t) = *reinterpret_cast<const u32x4*>(&st.o[cl][tv]);
+        for (int r = 0; r < 4; ++r) v[r] = APPLY ? softplus_f32(acc[m][r] + bias[m]) : acc[m][r];
+        IoT* dst = &st.o[w][16 * m + r16][16 * q + 4 * G];
+        if constexpr (sizeof(IoT) == 2) {
+          const uint32_t lo = Io<bf16_t>::from_f32(v[0]).bits | (uint32_t(Io<bf16_t>::from_f32(v[1]).bits) << 16);
+          const uint32_t hi = Io<bf16_t>::from_f32(v[2]).bits | (uint32_t(Io<bf16_t>::from_f32(v[3]).bits) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
-          for (int x = 0; x < E && t + x < L; ++x) out[c * L + t + x] = st.o[cl][tv + x];
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
+    }
+    // the wave's 32 x 64 tile, written above by this wave (its LDS accesses
+    // complete in order), leaves in rows: OV lanes cover one channel's 64 tokens
+    IoT* __restrict__ out = Oall + b * C * L;
+#pragma unroll
+    for (int v = 0; v < kProjWaveC * OV / 64; ++v) {
+      const int e = l + 64 * v;
+      const int row = e / OV, tv = (e - row * OV) * E;
+      const int64_t c = c0 + row, t = t0 + tv;
+      if (c < C && t < L)  // L is a whole number of 16-byte vectors
+        *reinterpret_cast<u32x4*>(out + c * L + t) = *reinterpret_cast<const u32x4*>(&st.o[w][row][tv]);
     }
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename IoT, int KCH>
-hipError_t launch_stream(const ProjParams& p, hipStream_t stream) {
-  const int64_t blocks = p.batch * ((p.channels + kProjC - 1) / kProjC);
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+hipError_t launch_tile(const ProjParams& p, hipStream_t stream) {
+  const int64_t units = p.batch * ((p.channels + kProjGroupC - 1) / kProjGroupC) *
+                        ((p.L + kProjStepT - 1) / kProjStepT);
+  int64_t resident = static_cast<int64_t>(device_cus()) * proj_blocks_per_cu<IoT, KCH>();
+  // SS_DT_PROJ_BLOCKS=n caps the grid at n blocks, read at every call (a
+  // tuning knob, and the way the tests give each block a long run of units
+  // across batch rows and channel groups)
+  if (const char* e = std::getenv("SS_DT_PROJ_BLOCKS")) {
+    const long v = std::atol(e);
+    if (v > 0 && v < resident) resident = v;
+  }
+  const int64_t blocks = units < resident ? units : resident;
   void* args[] = {const_cast<ProjParams*>(&p)};
-  const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_stream_kernel<IoT, KCH, true>)
-                           : reinterpret_cast<const void*>(&dt_proj_stream_kernel<IoT, KCH, false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kProjThreads), args, 0, stream);
+  const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_tile_kernel<IoT, KCH, true>)
+                           : reinterpret_cast<const void*>(&dt_proj_tile_kernel<IoT, KCH, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kProjWaves), args, 0, stream);
 }
 
 template <typename IoT>
@@ -404,19 +473,19 @@ hipError_t launch_proj_io(const ProjParams& p, hipStream_t stream) {
   constexpr int KC = 4 * E;
   const bool vec = p.R % E == 0 && reinterpret_cast<uintptr_t>(p.w_dt) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(p.delta) % 16 == 0;
-  // the streaming kernel also needs whole 16-byte output rows
+  // the tiled kernel also needs whole 16-byte output rows
   const bool rows16 = p.L % E == 0 && reinterpret_cast<uintptr_t>(p.dt) % 16 == 0;
   const int64_t kch = (p.R + KC - 1) / KC;
   if (vec && rows16 && kch <= 8) {
     switch (kch) {
-      case 1: return launch_stream<IoT, 1>(p, stream);
-      case 2: return launch_stream<IoT, 2>(p, stream);
-      case 3: return launch_stream<IoT, 3>(p, stream);
-      case 4: return launch_stream<IoT, 4>(p, stream);
-      case 5: return launch_stream<IoT, 5>(p, stream);
-      case 6: return launch_stream<IoT, 6>(p, stream);
-      case 7: return launch_stream<IoT, 7>(p, stream);
-      default: return launch_stream<IoT, 8>(p, stream);
+      case 1: return launch_tile<IoT, 1>(p, stream);
+      case 2: return launch_tile<IoT, 2>(p, stream);
+      case 3: return launch_tile<IoT, 3>(p, stream);
+      case 4: return launch_tile<IoT, 4>(p, stream);
+      case 5: return launch_tile<IoT, 5>(p, stream);
+      case 6: return launch_tile<IoT, 6>(p, stream);
+      case 7: return launch_tile<IoT, 7>(p, stream);
+      default: return launch_tile<IoT, 8>(p, stream);
     }
   }
   return vec ? launch_proj_vec<IoT, true>(p, stream) : launch_proj_vec<IoT, false>(p, stream);

@@ -81,8 +81,8 @@ PROJ_CASES = [
     ("bf16", 1, 65, 33, 20, True),
     ("f32", 1, 16, 16, 7, False),
     ("f32", 1, 33, 130, 64, True),
-    ("bf16", 1, 100, 200, 64, True),     # streaming form: channel and token tails
-    ("f32", 2, 64, 96, 128, False),      # streaming form: 8 chunks of k
+    ("bf16", 1, 100, 200, 64, True),     # tiled form: channel and token tails
+    ("f32", 2, 64, 96, 128, False),      # tiled form: 8 chunks of k
     ("bf16", 1, 70, 72, 256, True),
 ]
 
@@ -98,6 +98,25 @@ def test_dt_proj_parity(io, batch, channels, L, R, apply):
     w, delta = np64(c["w_dt"]), np64(c["delta"])
     ref = oracle.dt_proj(w, delta, dt_bias=np64(c["dt_bias"]), apply_softplus=apply)
     scale = np.stack([np.abs(w) @ np.abs(delta[b]).T for b in range(batch)])
+    check(dt, ref, scale, R, dt.dtype, "dt")
+
+
+@pytest.mark.parametrize("io,R", [("bf16", 160), ("f32", 64)])
+def test_dt_proj_long_runs(io, R, monkeypatch):
+    """The tiled form with its grid capped at 7 blocks (SS_DT_PROJ_BLOCKS), so
+    that every block walks a long run of (batch row, 256-channel group,
+    64-token) units, crossing batch rows, channel groups (the last one
+    partial: 600 = 2 x 256 + 88) and the partial last token unit (1000 = 15 x
+    64 + 40); every output against the oracle."""
+    print(f"dt_proj long runs io={io} R={R}", flush=True)
+    monkeypatch.setenv("SS_DT_PROJ_BLOCKS", "7")
+    c = make_producer_case(1560 + R, 2, 600, 1000, 4, R, io)
+    d = dev(c)
+    dt = ss.ss_dt_proj(d["w_dt"], d["delta"], d["dt_bias"], apply_softplus=True)
+    torch.cuda.synchronize()
+    w, delta = np64(c["w_dt"]), np64(c["delta"])
+    ref = oracle.dt_proj(w, delta, dt_bias=np64(c["dt_bias"]), apply_softplus=True)
+    scale = np.stack([np.abs(w) @ np.abs(delta[b]).T for b in range(2)])
     check(dt, ref, scale, R, dt.dtype, "dt")
 
 
@@ -146,7 +165,7 @@ def test_chain_into_the_scan(io):
 
 
 def test_producer_edges():
-    """Zero-size calls are no-ops; a rank beyond the streaming form (300 > 8
+    """Zero-size calls are no-ops; a rank beyond the tiled form (300 > 8
     chunks of 32) and a row length that is not a whole vector take the
     general path; width 8 with a reset on every token reads only the token
     itself."""
