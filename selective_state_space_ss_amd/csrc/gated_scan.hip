@@ -135,6 +135,19 @@ __device__ __forceinline__ v4f mfma32(const u32x4 a, const u32x4 b, v4f c) {
                                                  0);
 }
 __device__ __forceinline__ u32x2 ld2w(const bf16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Four rows of one column of a row-major bf16 tile, through the gfx950
+// transposing LDS read: in each 16-lane group, lane 4 r + q names 4
+// consecutive elements (q-th group of 4 columns) of the group's row r, and
+// lane c receives column c of those 4 x 16 elements, rows 0..3 (element 0 in
+// the low half of the first dword). The caller passes, for lane c16, the
+// address of element 4 (c16 mod 4) of row c16 / 4.
+__device__ __forceinline__ u32x2 ld_col4(const bf16_t* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4* lds_s4;
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ u32x4 cat(const u32x2 a, const u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
 
 template <typename E, int RT>
@@ -163,7 +176,8 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
   // Y = (A o L) V: M[t][4 G + r] in register r is the A operand of token
   // slots 4 G .. 4 G + 3; v of those tokens for this column from the grouped v
   const v4f mt = At * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
-  const u32x2 vraw = ld2w(&s.vg[G * St::VGS + (16 * w + c16) * 4]);
+  // v of tokens 4 G .. 4 G + 3 for this lane's column (the B operand)
+  const u32x2 vraw = ld_col4(&s.v[4 * G + (c16 >> 2)][16 * w + 4 * (c16 & 3)]);
   const Split4 ms = split4(mt);
   v4f Y = {0.0f, 0.0f, 0.0f, 0.0f};
   Y = mfma16(ms.hi, vraw, Y);
@@ -199,7 +213,8 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
   const float p15 = s.P[kT - 1];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const u32x2 kt = ld2w(&s.kg[G * St::KGS + (16 * rt + c16) * 4]);
+    // k of tokens 4 G .. 4 G + 3 for row 16 rt + c16 (the A operand)
+    const u32x2 kt = ld_col4(&s.k[4 * G + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
     S[rt] *= p15;
     S[rt] = mfma16(kt, ws.hi, S[rt]);
     S[rt] = mfma16(kt, ws.mid, S[rt]);
@@ -215,10 +230,13 @@ struct Stage {
   static constexpr int QS = DKP + 32 / (int)sizeof(E);    // row stride of q, k
   static constexpr int KGS = 4 * DKP + 64;                // group stride of the grouped k
   static constexpr int VGS = 4 * kCols + 64;              // group stride of the grouped v
+  static constexpr bool kGrouped = sizeof(E) == 4;      // fp32: token-grouped copies of k and v
+  static constexpr int VS = kCols + 16 / (int)sizeof(E);  // row stride of the row-major v (bf16)
   E q[kT][QS];
   E k[kT][QS];
-  E kg[4 * KGS];  // k[t][i] at [t / 4][i][t % 4]
-  E vg[4 * VGS];  // v[t][j] at [t / 4][j][t % 4]
+  E kg[kGrouped ? 4 * KGS : 1];  // fp32: k[t][i] at [t / 4][i][t % 4]
+  E vg[kGrouped ? 4 * VGS : 1];  // fp32: v[t][j] at [t / 4][j][t % 4]
+  alignas(16) E v[kGrouped ? 1 : kT][VS];  // bf16: v row-major (read by columns with the transposing load)
   float L[kT][kLS];
   float P[kT];
   E y[kT][kCols + 16 / sizeof(E)];  // the chunk's y, stored one chunk later as whole rows
@@ -327,15 +345,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
           const int i = (e - t * (DKP / VEC_E)) * VEC_E;
           *reinterpret_cast<u32x4*>(&s.q[t][i]) = qr[n];
           *reinterpret_cast<u32x4*>(&s.k[t][i]) = kr[n];
+          if constexpr (St::kGrouped) {
 #pragma unroll
-          for (int x = 0; x < VEC_E; ++x) s.kg[(t >> 2) * St::KGS + (i + x) * 4 + (t & 3)] = elem<IoT>(kr[n], x);
+            for (int x = 0; x < VEC_E; ++x) s.kg[(t >> 2) * St::KGS + (i + x) * 4 + (t & 3)] = elem<IoT>(kr[n], x);
+          }
         }
       }
       if (tid < VV) {
         const int t = tid / (kCols / VEC_E);
         const int j = (tid - t * (kCols / VEC_E)) * VEC_E;
+        if constexpr (St::kGrouped) {
 #pragma unroll
-        for (int x = 0; x < VEC_E; ++x) s.vg[(t >> 2) * St::VGS + (j + x) * 4 + (t & 3)] = elem<IoT>(vr, x);
+          for (int x = 0; x < VEC_E; ++x) s.vg[(t >> 2) * St::VGS + (j + x) * 4 + (t & 3)] = elem<IoT>(vr, x);
+        } else {
+          *reinterpret_cast<u32x4*>(&s.v[t][j]) = vr;
+        }
       }
     } else {
       for (int e = tid; e < kT * DKP; e += kThreads) {
@@ -345,12 +369,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
         const IoT kv = in ? kgp[(t0 + t) * dk + i] : zero_elem<IoT>();
         s.q[t][i] = qv;
         s.k[t][i] = kv;
-        s.kg[(t >> 2) * St::KGS + i * 4 + (t & 3)] = kv;
+        if constexpr (St::kGrouped) s.kg[(t >> 2) * St::KGS + i * 4 + (t & 3)] = kv;
       }
       for (int e = tid; e < kT * kCols; e += kThreads) {
         const int t = e / kCols, j = e - t * kCols;
         const bool in = t0 + t < L && jb + j < dv;
-        s.vg[(t >> 2) * St::VGS + j * 4 + (t & 3)] = in ? vgp[(t0 + t) * dv + jb + j] : zero_elem<IoT>();
+        const IoT vv = in ? vgp[(t0 + t) * dv + jb + j] : zero_elem<IoT>();
+        if constexpr (St::kGrouped) s.vg[(t >> 2) * St::VGS + j * 4 + (t & 3)] = vv;
+        else s.v[t][j] = vv;
       }
     }
     // Thread 16 t + u holds gamma_u. Over each 16-lane row (one t), the
