@@ -106,6 +106,12 @@ struct Split4 {
   u32x2 hi, mid, lo;  // four bf16 values each, two per dword (element 0 low)
 };
 
+// The high halves of two words as one word (a's in the low half): one
+// v_perm_b32, so the low halves need not be cleared first.
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 __device__ __forceinline__ Split4 split4(const v4f x) {
   uint32_t h[4], m[4], l[4];
 #pragma unroll
@@ -114,15 +120,17 @@ __device__ __forceinline__ Split4 split4(const v4f x) {
     const uint32_t hb = __builtin_bit_cast(uint32_t, xe) & 0xffff0000u;
     const float r = xe - __builtin_bit_cast(float, hb);
     const uint32_t mb = __builtin_bit_cast(uint32_t, r) & 0xffff0000u;
+    // r has at most 16 significant bits and mid holds its top 8, so the rest
+    // has at most 8: a bf16 value as it stands (its low half is zero)
     const float r2 = r - __builtin_bit_cast(float, mb);
     h[e] = hb;
     m[e] = mb;
-    l[e] = __builtin_bit_cast(uint32_t, r2) & 0xffff0000u;
+    l[e] = __builtin_bit_cast(uint32_t, r2);
   }
   Split4 o;
-  o.hi = u32x2{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]};
-  o.mid = u32x2{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]};
-  o.lo = u32x2{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3]};
+  o.hi = u32x2{pack_hi(h[0], h[1]), pack_hi(h[2], h[3])};
+  o.mid = u32x2{pack_hi(m[0], m[1]), pack_hi(m[2], m[3])};
+  o.lo = u32x2{pack_hi(l[0], l[1]), pack_hi(l[2], l[3])};
   return o;
 }
 
