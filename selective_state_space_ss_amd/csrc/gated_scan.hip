@@ -180,7 +180,6 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
     const int i = 16 * (RT - 1) + 4 * G;
     At = mfma16(ld2w(&s.k[c16][i]), ld2w(&s.q[c16][i]), At);
   }
-  __builtin_amdgcn_sched_barrier(0);
   // Y = (A o L) V: M[t][4 G + r] in register r is the A operand of token
   // slots 4 G .. 4 G + 3; v of those tokens for this column from the grouped v
   const v4f mt = At * *reinterpret_cast<const v4f*>(&s.L[c16][4 * G]);
@@ -191,7 +190,6 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
   Y = mfma16(ms.hi, vraw, Y);
   Y = mfma16(ms.mid, vraw, Y);
   Y = mfma16(ms.lo, vraw, Y);
-  __builtin_amdgcn_sched_barrier(0);
   // Z = Q S_prev: rows 16 rt + 4 G + r of S are the B operand of index slots
   // 4 G + r of tile rt; two tiles per 32-index MFMA
   v4f Z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -202,7 +200,6 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
     Z = mfma32(qa, cat(s0.hi, s1.hi), Z);
     Z = mfma32(qa, cat(s0.mid, s1.mid), Z);
     Z = mfma32(qa, cat(s0.lo, s1.lo), Z);
-    __builtin_amdgcn_sched_barrier(0);  // one pair's split terms live at a time
   }
   if constexpr (RT % 2 == 1) {
     const u32x2 qa = ld2w(&s.q[c16][16 * (RT - 1) + 4 * G]);
@@ -227,7 +224,6 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
     S[rt] = mfma16(kt, ws.hi, S[rt]);
     S[rt] = mfma16(kt, ws.mid, S[rt]);
     S[rt] = mfma16(kt, ws.lo, S[rt]);
-    __builtin_amdgcn_sched_barrier(0);
   }
   return Y;
 }
