@@ -287,6 +287,22 @@ def measure_producers(ss, stream, reps: int = 20):
     return res
 
 
+COPY_CEILING_BYTES = 1 << 30   # each way
+
+
+def measure_copy(stream, reps: int = 20):
+    """A plain device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB), the
+    achievable streaming rate on this machine next to the 8 TB/s peak."""
+    import torch
+    src = torch.empty(COPY_CEILING_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    us = time_launches(lambda: dst.copy_(src), stream, reps)
+    moved = 2 * COPY_CEILING_BYTES
+    del src, dst
+    return {"bytes_moved": moved, "us": round(us, 2), "GB_s": round(moved / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(moved / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(inp, w, budget_s: float):
     """The oracle over whole (b, c) rows of the prompt workload, row blocks of
     every batch row in turn, until the time budget is spent."""
@@ -449,7 +465,8 @@ def main():
         out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream),
                          "ss_gated_scan": measure_gated(ss, stream),
                          "ss_effective_attention": measure_attention(ss, stream),
-                         "producers": measure_producers(ss, stream)}
+                         "producers": measure_producers(ss, stream),
+                         "stream_copy_1GiB": measure_copy(stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
