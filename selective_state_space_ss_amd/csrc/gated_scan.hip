@@ -28,9 +28,11 @@
 // between waves).
 //
 // Staging. The block stages a chunk in LDS, double buffered with one barrier
-// per chunk: q and k row-major (operands of q k^T and q S), and k and v in
-// 4-token groups [t / 4][row][t % 4] (the operands that contract over tokens
-// need 4 consecutive tokens of one row per lane), plus L and P. The next
+// per chunk: q and k row-major (operands of q k^T and q S), v, plus L and P.
+// The operands that contract over tokens need 4 consecutive tokens of one
+// column of k or v per lane: with bf16 I/O they are read from the row-major
+// tiles with the transposing LDS load (ld_col4); with fp32 I/O k and v are
+// also staged in 4-token groups [t / 4][row][t % 4]. The next
 // chunk's q, k, v are loaded into registers with 16-byte loads, and its gamma
 // one token per lane, while the current chunk is computed (no scalar loads in
 // the loop: they would share the LDS wait counter). Inputs whose rows are not
