@@ -110,6 +110,7 @@ __device__ __forceinline__ float silu_f32(float z) {
 // DPP control words (gfx9 encoding).
 constexpr int kDppRowShl1 = 0x101;  // row_shl:k is kDppRowShl1 + k - 1: lane i reads lane i + k
 constexpr int kDppRowShr1 = 0x111;  // row_shr:1: lane i reads lane i - 1
+constexpr int kDppRowNewBcast0 = 0x150;   // lane 0 of each row to its whole row
 constexpr int kDppRowNewBcast15 = 0x15F;  // lane 15 of each row to its whole row
 constexpr int kDppQuadXor1 = 0xB1;        // quad_perm:[1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;        // quad_perm:[2,3,0,1]

@@ -110,6 +110,7 @@ struct AttnParams {
   const float* dt_bias; // [channels] or nullptr
   int dt_softplus, include_dt, per_state;
   float* M;             // [batch, channels, L, L] or [batch, channels, N, L, L]
+  int out_vec;          // rows of M are whole 16-byte vectors (set by the launcher)
 };
 
 hipError_t launch_effective_attention(const AttnParams& p, bool io_bf16, hipStream_t stream);

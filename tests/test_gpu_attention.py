@@ -67,6 +67,8 @@ CASES = [
     ("bf16", 1, 2, 64, 257, True, True, False),
     ("f32", 1, 2, 8, 513, True, True, False),
     ("bf16", 3, 1, 16, 1, True, False, False),
+    ("bf16", 1, 2, 16, 512, True, True, False),   # the tiled form's longest sequence (32 row tiles)
+    ("f32", 2, 3, 12, 48, False, False, False),   # three whole tiles, softplus off
 ]
 
 
