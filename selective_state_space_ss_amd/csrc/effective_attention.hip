@@ -36,15 +36,6 @@ namespace {
 
 constexpr int kTile = 64;    // rows per staged tile
 
-// M is written once and not read again by the kernel: its stores carry the
-// nontemporal hint (at 1 x 1536 x 16 x 256 this took the tiled form from 104
-// to 87 us; the every-token states kernel measured slower with the same hint
-// and keeps plain stores).
-__device__ __forceinline__ void stream_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
-__device__ __forceinline__ void stream_store4(float4 v, float* p) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4*>(p));
-}
 constexpr int kThreads = 256;
 constexpr int kCols = 256;   // columns per block
 
@@ -357,7 +348,7 @@ effective_attention_tiles_kernel(const AttnParams p) {
             const float4 o = *reinterpret_cast<const float4*>(&sO[w][rr][cc]);
             float* dst = Mb + (i0 + rr) * L + q * kMT + cc;
             if (p.out_vec) {
-              stream_store4(o, dst);
+              stream_store16(o, dst);
             } else {
               stream_store(o.x, dst); stream_store(o.y, dst + 1); stream_store(o.z, dst + 2); stream_store(o.w, dst + 3);
             }
@@ -373,7 +364,7 @@ effective_attention_tiles_kernel(const AttnParams p) {
       float* row = Mb + (i0 + rr) * L;
       if (p.out_vec) {
         for (int64_t jz = z0 + 4 * lane; jz < L; jz += 256)
-          stream_store4(make_float4(0.0f, 0.0f, 0.0f, 0.0f), row + jz);
+          stream_store16(make_float4(0.0f, 0.0f, 0.0f, 0.0f), row + jz);
       } else {
         for (int64_t jz = z0 + lane; jz < L; jz += 64) stream_store(0.0f, row + jz);
       }

@@ -396,7 +396,7 @@ void dt_proj_tile_kernel(const ProjParams p) {
       const int row = e / OV, tv = (e - row * OV) * E;
       const int64_t c = c0 + row, t = t0 + tv;
       if (c < C && t < L)  // L is a whole number of 16-byte vectors
-        *reinterpret_cast<u32x4*>(out + c * L + t) = *reinterpret_cast<const u32x4*>(&st.o[w][row][tv]);
+        stream_store16(*reinterpret_cast<const uint4*>(&st.o[w][row][tv]), out + c * L + t);
     }
   }
 }

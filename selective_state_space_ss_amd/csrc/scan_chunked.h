@@ -301,6 +301,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
               const int tok = 64 * q + 4 * tl;  // within the chunk
               const float4 v4 = *reinterpret_cast<const float4*>(&sSt[wave * kRowsPerWave + row][(tok / K) * KP + tok % K]);
               if (full && p.states_vec) {
+                // (plain stores: with the streaming hint this pattern measured slower)
                 *reinterpret_cast<float4*>(dst + tok) = v4;
               } else {
                 const float hv[4] = {v4.x, v4.y, v4.z, v4.w};

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(const UpdatePara
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       if constexpr (VEC) {
-        *reinterpret_cast<float4*>(sg + r * N + coord(k, 0)) =
-            make_float4(s[j][4 * k], s[j][4 * k + 1], s[j][4 * k + 2], s[j][4 * k + 3]);
+        stream_store16(make_float4(s[j][4 * k], s[j][4 * k + 1], s[j][4 * k + 2], s[j][4 * k + 3]),
+                       sg + r * N + coord(k, 0));
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
