@@ -8,7 +8,14 @@
 // (softplus(dt + dt_bias) or dt + dt_bias); optionally column j scaled by
 // dt[b, c, j], or the terms kept per state coordinate n.
 //
-// Work and bound. Every (i, j) element of the lower triangle needs the N
+// Two kernels. The summed matrix with N <= 16 and L <= 512 takes the tiled
+// form further below: the tiles left of the diagonal as fp32 matrix-core
+// contractions of prefix, gap and suffix products of the decay factors. The
+// per-coordinate matrix, and larger N or L, take the column walk described
+// here. Both are bound by writing M, and M's stores carry the nontemporal
+// hint (M is written once and never read back).
+//
+// Column walk. Every (i, j) element of the lower triangle needs the N
 // running products of its column, so a lane owns one column j and carries
 // d[n] = B[b, n, j] (* dt_j) * prod_{k=j+1..i} exp(A[c, n] dt_k) down the
 // rows: one multiply to extend each product and one FMA to contract it with
