@@ -379,8 +379,8 @@ void dt_proj_tile_kernel(const ProjParams p) {
         for (int r = 0; r < 4; ++r) v[r] = APPLY ? softplus_f32(acc[m][r] + bias[m]) : acc[m][r];
         IoT* dst = &st.o[w][16 * m + r16][16 * q + 4 * G];
         if constexpr (sizeof(IoT) == 2) {
-          const uint32_t lo = Io<bf16_t>::from_f32(v[0]).bits | (uint32_t(Io<bf16_t>::from_f32(v[1]).bits) << 16);
-          const uint32_t hi = Io<bf16_t>::from_f32(v[2]).bits | (uint32_t(Io<bf16_t>::from_f32(v[3]).bits) << 16);
+          const uint32_t lo = pack_bf16x2(v[0], v[1]);
+          const uint32_t hi = pack_bf16x2(v[2], v[3]);
           *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);

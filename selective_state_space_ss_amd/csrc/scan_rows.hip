@@ -64,8 +64,7 @@ struct Tiling {
 
 // Two consecutive fp32 values stored as an aligned pair of I/O elements.
 __device__ __forceinline__ void store_pair(bf16_t* p, float a, float b) {
-  const uint32_t w = uint32_t(Io<bf16_t>::from_f32(a).bits) | (uint32_t(Io<bf16_t>::from_f32(b).bits) << 16);
-  *reinterpret_cast<uint32_t*>(p) = w;
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
 }
 __device__ __forceinline__ void store_pair(float* p, float a, float b) {
   *reinterpret_cast<float2*>(p) = make_float2(a, b);

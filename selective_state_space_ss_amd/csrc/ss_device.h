@@ -35,6 +35,14 @@ struct Io<bf16_t> {
   }
 };
 
+// Two fp32 values rounded to nearest even as bf16 and packed (lo in the low
+// half): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // Load kVec consecutive elements (16 bytes) and widen to fp32.
 __device__ __forceinline__ void load_vec16(const float* p, float* out) {
   const float4 v = *reinterpret_cast<const float4*>(p);
@@ -91,9 +99,7 @@ __device__ __forceinline__ void store_vec16(bf16_t* p, const float* v) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = Io<bf16_t>::from_f32(v[2 * i]).bits;
-    const uint32_t hi = Io<bf16_t>::from_f32(v[2 * i + 1]).bits;
-    w[i] = lo | (hi << 16);
+    w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
   }
   stream_store16(make_uint4(w[0], w[1], w[2], w[3]), p);
 }
