@@ -349,8 +349,9 @@ def main():
         summarize_traffic(*args.summarize_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the scan shards over batch and "
-              "channels with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the scan would shard over "
+              "batch rows and channels, which exchange nothing, so one GPU's share is the measured case)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import selective_state_space_ss_amd as ss

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine; without a device they are skipped, not failed.
+    # GPU tests need an MI355X; without a device they are skipped, not failed.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
