@@ -93,3 +93,124 @@ def test_dt_proj_past_2_31_outputs():
     free()
     dr = oracle.dt_proj(np64(w_dt[ROWS]), np64(ds), np64(bias[ROWS]), apply_softplus=True)
     check_close(np64(dg), dr[0], *TOL["bf16"], "dt_proj past 2^31")
+
+
+def test_decode_state_past_2_31_elements():
+    Bn, Cn = 4096, 32776
+    assert Bn * Cn * N > 2 ** 31
+    print(f"large decode {Bn} x {Cn} x {N} bf16 gate, fp32 state", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(41)
+    state = torch.randn((Bn, Cn, N), generator=g, device="cuda", dtype=torch.float32)
+    x, dt, z = big_normal(42, (Bn, Cn)), big_normal(43, (Bn, Cn)), big_normal(44, (Bn, Cn))
+    Bm = cpu_normal(45, (Bn, N)).to(torch.bfloat16)
+    Cm = cpu_normal(46, (Bn, N)).to(torch.bfloat16)
+    A = s4d_real_A(Cn, N)
+    D = cpu_normal(47, (Cn,))
+    dt_bias = cpu_normal(48, (Cn,), -4.0, 0.5)
+    bs, cs = [0, 1, Bn - 1], [0, 17, Cn - 1]
+    sub = lambda t: t[bs][:, cs].cpu()
+    s_before = sub(state)
+    y = ss.ss_state_update(state, x, dt, A.cuda(), Bm.cuda(), Cm.cuda(), D=D.cuda(), z=z, dt_bias=dt_bias.cuda())
+    torch.cuda.synchronize()
+    s_after, yg, xs, dts, zs = sub(state), sub(y), sub(x), sub(dt), sub(z)
+    del state, x, dt, z, y
+    free()
+    yr, sr = oracle.state_update(np64(s_before), np64(xs), np64(dts), np64(A[cs]), np64(Bm[bs]), np64(Cm[bs]),
+                                 D=np64(D[cs]), z=np64(zs), dt_bias=np64(dt_bias[cs]))
+    check_close(np64(yg), yr, *TOL["bf16"], "decode y past 2^31")
+    check_close(np64(s_after), sr, *TOL_STATE, "decode state past 2^31")
+
+
+def test_every_token_states_past_2_31_elements():
+    Cn, Ls = 64, 2 ** 21 + 8
+    assert Cn * N * Ls > 2 ** 31
+    print(f"large states {BATCH} x {Cn} x {N} x {Ls} bf16 gate h0", flush=True)
+    x, dt, z = big_normal(51, (BATCH, Cn, Ls)), big_normal(52, (BATCH, Cn, Ls)), big_normal(53, (BATCH, Cn, Ls))
+    Bm = cpu_normal(54, (BATCH, N, Ls)).to(torch.bfloat16)
+    Cm = cpu_normal(55, (BATCH, N, Ls)).to(torch.bfloat16)
+    A = s4d_real_A(Cn, N)
+    D = cpu_normal(56, (Cn,))
+    dt_bias = cpu_normal(57, (Cn,), -4.0, 0.5)
+    h0 = cpu_normal(58, (BATCH, Cn, N), 0.0, 0.1)
+    y, h, st = ss.ss_scan_fwd_states(x, dt, A.cuda(), Bm.cuda(), Cm.cuda(), D=D.cuda(), z=z, dt_bias=dt_bias.cuda(),
+                                     h0=h0.cuda())
+    torch.cuda.synchronize()
+    assert st.numel() > 2 ** 31
+    rows = [0, Cn - 1]
+    stg, yg, hg = st[0, rows].cpu(), y[0, rows].cpu(), h[0, rows].cpu()
+    xs, dts, zs = x[:, rows].cpu(), dt[:, rows].cpu(), z[:, rows].cpu()
+    del x, dt, z, y, h, st
+    free()
+    yr, hr, sr = oracle.scan(np64(xs), np64(dts), np64(A[rows]), np64(Bm), np64(Cm), D=np64(D[rows]), z=np64(zs),
+                             dt_bias=np64(dt_bias[rows]), h0=np64(h0[:, rows]), return_states=True)
+    check_close(np64(yg), yr[0], *TOL["bf16"], "states-scan y past 2^31")
+    check_close(np64(hg), hr[0], *TOL_STATE, "states-scan h_last past 2^31")
+    check_close(np64(stg), sr[0].transpose(0, 2, 1), *TOL_STATE, "every-token states past 2^31")
+
+
+@pytest.mark.parametrize("per_state", [False, True], ids=["summed", "per_state"])
+def test_effective_attention_past_2_31_elements(per_state):
+    Cn, La, W = (2, 8200, 256) if per_state else (32, 8200, 256)
+    assert Cn * (N if per_state else 1) * La * La > 2 ** 31
+    print(f"large effective attention {BATCH} x {Cn} x {N} x {La} bf16 per_state={per_state}", flush=True)
+    dt = big_normal(61, (BATCH, Cn, La))
+    Bm = cpu_normal(62, (BATCH, N, La)).to(torch.bfloat16)
+    Cm = cpu_normal(63, (BATCH, N, La)).to(torch.bfloat16)
+    A = s4d_real_A(Cn, N)
+    dt_bias = cpu_normal(64, (Cn,), -4.0, 0.5)
+    M = ss.ss_effective_attention(dt, A.cuda(), Bm.cuda(), Cm.cuda(), dt_bias.cuda(), per_state_coord=per_state)
+    torch.cuda.synchronize()
+    assert M.numel() > 2 ** 31
+    c = Cn - 1
+    head, tail = slice(0, W), slice(La - W, La)
+    Mc = M[0, c]
+    blocks = {k: Mc[..., r, s].cpu() for k, (r, s) in
+              {"head": (head, head), "tail": (tail, tail), "corner": (tail, head), "upper": (head, tail)}.items()}
+    dts = dt[0, c].cpu()
+    del M, Mc, dt
+    free()
+    # M[i, j] involves only the tokens j .. i, so a diagonal block is the
+    # oracle's matrix of that window of tokens
+    for name, win in (("head", head), ("tail", tail)):
+        d = np64(dts[win]).reshape(1, 1, W)
+        kw = dict(dt_bias=np64(dt_bias[c:c + 1]), per_state_coord=per_state)
+        ref = oracle.effective_attention(d, np64(A[c:c + 1]), np64(Bm[:, :, win]), np64(Cm[:, :, win]), **kw)[0, 0]
+        scale = np.abs(oracle.effective_attention(d, np64(A[c:c + 1]), np.abs(np64(Bm[:, :, win])),
+                                                  np.abs(np64(Cm[:, :, win])), **kw)[0, 0])
+        g = np64(blocks[name])
+        err = np.abs(g - ref)
+        bound = 1e-4 * np.abs(ref) + 1e-5 + (W + 2 * N) * 2.0 ** -24 * scale
+        assert np.isfinite(g).all() and (err <= bound).all(), f"{name} block: worst {(err - bound).max()}"
+    # above the diagonal: exact zeros; far below it the decay over ~8000 tokens
+    # is below fp32's range (the oracle's value there is under 1e-30)
+    assert (blocks["upper"] == 0).all()
+    assert (blocks["corner"].abs() <= 1e-30).all()
+
+
+def test_gated_scan_past_2_31_elements():
+    Bh, Lg, dk, dv = 128, 131_080, 128, 64
+    assert Bh * Lg * dk > 2 ** 31
+    print(f"large gated scan {Bh} x {Lg} x {dk} x {dv} bf16", flush=True)
+    q = big_normal(71, (Bh, Lg, dk)) * dk ** -0.5
+    k = big_normal(72, (Bh, Lg, dk)) * dk ** -0.5
+    v = big_normal(73, (Bh, Lg, dv))
+    g = torch.Generator(device="cuda").manual_seed(74)
+    gamma = torch.rand((Bh, Lg), generator=g, device="cuda") * 0.1 + 0.9
+    s0 = cpu_normal(75, (Bh, dk, dv))
+    y, fs = ss.ss_gated_scan(q, k, v, gamma, s0.cuda())
+    torch.cuda.synchronize()
+    h = Bh - 1
+    qs, ks, vs, gs = q[h:].cpu(), k[h:].cpu(), v[h:].cpu(), gamma[h:].cpu()
+    yg, fg = y[h:].cpu(), fs[h:].cpu()
+    del q, k, v, gamma, y, fs
+    free()
+    args = [np64(t) for t in (qs, ks, vs, gs)]
+    yr, fr = oracle.gated_scan(*args, s0=np64(s0[h:]))
+    ya, fa = oracle.gated_scan(*[np.abs(a) for a in args], s0=np.abs(np64(s0[h:])))
+    # y in bf16, the final state in fp32: the gated tests' bound, rtol |r| + atol + 2^-19 S
+    for got, ref, ref_abs, (rtol, atol), what in ((yg, yr, ya, TOL["bf16"], "y"),
+                                                  (fg, fr, fa, TOL["f32"], "final state")):
+        gg = np64(got)
+        err = np.abs(gg - ref)
+        bound = rtol * np.abs(ref) + atol + 2.0 ** -19 * np.abs(ref_abs)
+        assert np.isfinite(gg).all() and (err <= bound).all(), f"gated {what} past 2^31: worst {(err - bound).max()}"
