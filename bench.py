@@ -78,15 +78,18 @@ SCAN_SOURCES = ("scan_fwd.hip", "scan_chunked.h", "ss_device.h", "ss_launch.h")
 
 
 def kernel_source_digest() -> str:
-    """Digest of the sources the prompt-scan kernel is compiled from: a
-    traffic figure is reported only while it matches (the kernel has not
-    changed since the counters were taken)."""
+    """Digest of the sources and compiler flags the prompt-scan kernel is
+    built from: a traffic figure is reported only while it matches (the
+    kernel has not changed since the counters were taken)."""
     import hashlib
+    from selective_state_space_ss_amd.build import HIPCC_FLAGS, SOURCE_FLAGS
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_ss_amd", "csrc")
     for name in SCAN_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    flags = [f for f in HIPCC_FLAGS if not f.startswith("/")] + SOURCE_FLAGS.get("scan_fwd.hip", [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,6 +29,14 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions. The chunked prompt scan is scheduled with LLVM's
+# iterative-ILP machine scheduler: on MI355X it measured 342 against 346.5 us
+# at batch 8 x 5120 channels x 2048 tokens and 85.7 against 89.0 us at
+# 4 x 1536 x 2048 (no change with resets), with identical results. It is set
+# for this file only: the other kernels were not measured with it, and this
+# toolchain's compiler aborts on gated_scan.hip under it.
+SOURCE_FLAGS = {"scan_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -53,7 +61,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        out = _run([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out:
             print(out)
         return obj
