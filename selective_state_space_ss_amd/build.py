@@ -29,13 +29,17 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-# Per-source additions. The chunked prompt scan is scheduled with LLVM's
-# iterative-ILP machine scheduler: on MI355X it measured 342 against 346.5 us
-# at batch 8 x 5120 channels x 2048 tokens and 85.7 against 89.0 us at
-# 4 x 1536 x 2048 (no change with resets), with identical results. It is set
-# for this file only: the other kernels were not measured with it, and this
-# toolchain's compiler aborts on gated_scan.hip under it.
-SOURCE_FLAGS = {"scan_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# Per-source additions. The chunked prompt scan and its states variants are
+# scheduled with LLVM's iterative-ILP machine scheduler. On MI355X it measured
+# 342 against 346.5 us at batch 8 x 5120 channels x 2048 tokens, 85.7 against
+# 89.0 us at 4 x 1536 x 2048 (no change with resets), and 360 against 374 us
+# (one selected state) and 1445 against 1456 us (every state) at the first
+# shape, with identical results. The other files keep the default: with it
+# the producers, the attention and the decode step measured no change, and
+# this toolchain's compiler aborts on gated_scan.hip (max-ilp made that
+# kernel 14 % slower).
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+SOURCE_FLAGS = {"scan_fwd.hip": _ILP, "scan_states.hip": _ILP}
 
 
 def hipcc() -> str:
