@@ -18,11 +18,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["chunked", "rows"])
+@pytest.fixture(params=["chunked", "chunked32", "rows"])
 def scan_kernel(request, monkeypatch):
-    """Both prompt-scan kernels (the library picks one by shape; the
-    SS_SCAN_KERNEL override, read at every call, forces one)."""
-    monkeypatch.setenv("SS_SCAN_KERNEL", request.param)
+    """Both prompt-scan kernels, the chunked one at 16 and at 32 tokens per
+    lane (the library picks by shape; the SS_SCAN_KERNEL and
+    SS_SCAN_TOKENS_PER_LANE overrides, read at every call, force one)."""
+    monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if request.param == "rows" else "chunked")
+    monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if request.param == "chunked32" else "16")
     return request.param
 
 
