@@ -16,10 +16,17 @@ value = whole-step algorithmic bytes / step time (GB/s). The per-kernel
 durations come from HIP events recorded around each launch on the stream the
 kernels run on.
 
-roofline: the prompt scan dominates and is bound by VALU issue (one
-transcendental and five FMA-class operations per token and state
-coordinate), so it is reported against the fp32 vector peak in
-FMA-equivalent work; see the FLOP model in roofline_flops().
+roofline: the prompt scan dominates the step. Its roofline is the larger of
+two times, as a fraction of the kernel time: the algorithmic bytes at the
+8 TB/s HBM peak, and the transcendentals the method needs (one exp2 per token
+and state coordinate for the decay, exp and log for the softplus, exp and rcp
+for the gate) at the transcendental rate measured on MI355X by the issue-rate
+probe (profiles/issue_rates_gfx950.json, written by --probe-issue). A second
+figure, issue_frac, prices the method's whole minimum VALU work (the
+transcendentals plus the FMA-class operations) at the probe's measured rates:
+on gfx950 an exp2 occupies the same VALU issue slots as ordinary fp32 work
+(about two FMA slots each; the probe finds no overlap), so that is the bound
+the kernel actually runs against.
 
 cpu_baseline: the fp64 CPU oracle (oracle/), unchanged, timed on this host's
 cores over a bounded sample of the prompt workload's rows.
@@ -35,21 +42,74 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
-TRANS_FLOP_EQ = 8.0        # one transcendental issues at 1/4 the FMA rate: 4 FMA slots = 8 flops
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 matrix / packed vector, published (the unpacked VALU issues half)
+ISSUE_FILE = os.path.join(ROOT, "profiles", "issue_rates_gfx950.json")
+# Nominal gfx950 rates, used only if the measured file is missing: per CU and
+# clock 64 fp32 FMA lanes (a wave64 VALU instruction every 4 clocks on each of
+# 4 SIMDs) and 32 exp2 lanes, 256 CUs at 2.4 GHz.
+NOMINAL_FMA_RATE = 64 * 256 * 2.4e9
+NOMINAL_EXP_RATE = 32 * 256 * 2.4e9
 
 
-def roofline_flops(w) -> float:
-    """FMA-equivalent arithmetic the scan needs per launch (FMA = 2, mul/add = 1,
-    transcendental = 8). Per token and state coordinate: dt*A (1), exp (8),
-    (dt x)*B (1), h = a h + b (2), y += C h (2) = 14. Per token: dt + bias (1),
-    softplus = exp + log (16) plus max/add (2), dt*x (1), y += D x (2); with
-    the gate silu = exp + rcp (16) plus add and two muls (3)."""
+def issue_rates():
+    """(fp32 FMA lane-ops/s, exp2 lane-ops/s, source) from the committed
+    probe measurement; the nominal rates if it is missing."""
+    try:
+        with open(ISSUE_FILE) as f:
+            r = json.load(f)
+        return r["fma_lane_ops_per_s"], r["exp2_lane_ops_per_s"], os.path.relpath(ISSUE_FILE, ROOT)
+    except (OSError, ValueError, KeyError):
+        return NOMINAL_FMA_RATE, NOMINAL_EXP_RATE, "nominal (64 FMA and 32 exp2 lanes per CU and clock, 2.4 GHz)"
+
+
+def scan_work(w):
+    """Algorithmic work of one prompt-scan launch of workload w.
+
+    bytes: every input read once and every output written once.
+    trans: transcendentals the method needs: per channel-token one exp2 per
+    state coordinate (the decay), exp and log (softplus), and exp and rcp
+    (the gate, when on).
+    fma: the other fp32 operations, in FMA-class instructions: per token and
+    state coordinate dt*A, (dt x)*B, h = a h + b, y += C h (4); per
+    channel-token dt + bias, the softplus' max, add and log scaling (3), dt*x,
+    y += D x (2) and, with the gate, 1 + e, z * r, y * silu (3)."""
+    from selective_state_space_ss_amd.workloads import algorithmic_bytes
     ct = w.batch * w.channels * max(w.seqlen, 1)
-    per_ct = 1 + 18 + 1 + 2 + (19 if w.gate else 0)
-    return float(ct) * (14.0 * w.state_dim + per_ct)
+    trans = ct * (w.state_dim + 2 + (2 if w.gate else 0))
+    fma = ct * (4 * w.state_dim + 6 + (3 if w.gate else 0))
+    return {"channel_tokens": ct, "bytes": algorithmic_bytes(w), "trans": trans, "fma": fma}
+
+
+def scan_roofline(w, us: float, rates) -> dict:
+    """Per-launch figures of a prompt scan that took `us` microseconds:
+    GB/s, channel-tokens/s, the HBM and transcendental fractions, frac =
+    max(HBM time, transcendental time) / kernel time, and issue_frac = the
+    method's minimum VALU time (transcendentals at the exp2 rate plus the
+    FMA-class work at the FMA rate, which share the issue slots) / kernel
+    time."""
+    fma_rate, exp_rate, _ = rates
+    wk = scan_work(w)
+    t = us * 1e-6
+    hbm_s = wk["bytes"] / (PEAK_HBM_GBS * 1e9)
+    exp_s = wk["trans"] / exp_rate
+    issue_s = exp_s + wk["fma"] / fma_rate
+    return {"us": round(us, 2), "GB_s": round(wk["bytes"] / t / 1e9, 1),
+            "channel_tokens_per_s": round(wk["channel_tokens"] / t, 1), "algorithmic_bytes": wk["bytes"],
+            "transcendentals": wk["trans"], "hbm_frac": round(hbm_s / t, 4), "exp_frac": round(exp_s / t, 4),
+            "frac": round(max(hbm_s, exp_s) / t, 4), "issue_frac": round(issue_s / t, 4)}
+
+
+def decode_roofline(w, us: float) -> dict:
+    """The decode update is bound by HBM: frac = algorithmic bytes at 8 TB/s /
+    kernel time."""
+    from selective_state_space_ss_amd.workloads import algorithmic_bytes
+    nbytes = algorithmic_bytes(w)
+    t = us * 1e-6
+    return {"us": round(us, 2), "GB_s": round(nbytes / t / 1e9, 1),
+            "channel_updates_per_s": round(w.batch * w.channels / t, 1), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ss_scan_fwd_mamba2p8b.json")
@@ -66,12 +126,69 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-token-states, gated-scan, effective-attention and producer measurements")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-configuration timings (tiny, Mamba-130M, packed reset, cold runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes into " + TRAFFIC_FILE)
+    ap.add_argument("--probe-issue", metavar="OUT_JSON",
+                    help="run the fp32 FMA / transcendental issue-rate probe, write its JSON to OUT_JSON, exit")
     return ap.parse_args()
+
+
+# (exp2 chains, FMA chains) per loop iteration of the issue-rate probe
+# (libssprobe.so); the pure kernels give the two peaks, the mixed ones show
+# whether the two kinds of work overlap.
+PROBE_MIXES = [(0, 8), (0, 16), (8, 0), (16, 0), (1, 8), (2, 8), (4, 8), (8, 8), (1, 4), (1, 5), (4, 4)]
+PROBE_BLOCKS, PROBE_ITERS, PROBE_THREADS = 2048, 32768, 256
+
+
+def measure_issue_rates():
+    """Lane operations per second of fp32 FMA and of the exp2 transcendental
+    on this GPU, each alone and mixed (2048 blocks of 256 threads, 8 waves per
+    SIMD, independent chains, no memory traffic). Returns a dict with the two
+    peaks (lane-ops/s and per CU per measured clock) and, for every mix, the
+    measured time against the no-overlap sum and the full-overlap max of the
+    pure rates."""
+    import ctypes
+    from selective_state_space_ss_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.ssprobe_issue.restype = ctypes.c_int
+    lib.ssprobe_issue.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_double)] * 2
+    lanes = PROBE_BLOCKS * PROBE_THREADS * PROBE_ITERS
+    runs = {}
+    for ne, nf in PROBE_MIXES:
+        ms, mhz = ctypes.c_double(), ctypes.c_double()
+        rc = lib.ssprobe_issue(ne, nf, PROBE_ITERS, PROBE_BLOCKS, ctypes.byref(ms), ctypes.byref(mhz))
+        if rc != 0:
+            raise RuntimeError(f"ssprobe_issue({ne}, {nf}) returned {rc}")
+        runs[(ne, nf)] = (ms.value * 1e-3, mhz.value)
+        print(f"probe exp2 x{ne} fma x{nf}: {ms.value:.3f} ms, clock {mhz.value:.0f} MHz", file=sys.stderr, flush=True)
+    fma_rate = max(lanes * nf / t for (ne, nf), (t, _) in runs.items() if ne == 0)
+    exp_rate = max(lanes * ne / t for (ne, nf), (t, _) in runs.items() if nf == 0)
+    clocks = sorted(m for _, m in runs.values() if m > 0)
+    mhz = clocks[len(clocks) // 2] if clocks else 0.0
+    cus = 256
+    per_clk = (lambda r: r / (cus * mhz * 1e6)) if mhz else (lambda r: None)
+    mixes = []
+    for (ne, nf), (t, m) in runs.items():
+        if ne and nf:
+            te, tf = lanes * ne / exp_rate, lanes * nf / fma_rate
+            mixes.append({"exp2_per_iter": ne, "fma_per_iter": nf, "s": t, "no_overlap_s": te + tf,
+                          "full_overlap_s": max(te, tf), "measured_over_no_overlap": round(t / (te + tf), 4)})
+    return {
+        "probe": "libssprobe.so ssprobe_issue: %d blocks x %d threads x %d iterations per kernel"
+                 % (PROBE_BLOCKS, PROBE_THREADS, PROBE_ITERS),
+        "fma_lane_ops_per_s": fma_rate,
+        "exp2_lane_ops_per_s": exp_rate,
+        "clock_mhz_measured": mhz,
+        "fma_lane_ops_per_cu_clk": per_clk(fma_rate),
+        "exp2_lane_ops_per_cu_clk": per_clk(exp_rate),
+        "exp2_cost_in_fma_slots": fma_rate / exp_rate,
+        "mixes": mixes,
+    }
 
 
 SCAN_SOURCES = ("scan_fwd.hip", "scan_chunked.h", "ss_device.h", "ss_launch.h")
@@ -290,6 +407,92 @@ def measure_producers(ss, stream, reps: int = 20):
     return res
 
 
+FLUSH_BYTES = 1 << 30
+
+
+def time_cold(f, stream, reps: int, flush) -> float:
+    """Average microseconds of f when the caches hold none of its data: before
+    each timed launch a read of the 1 GiB `flush` tensor (a sum) streams
+    through the L2s and the 256 MB last-level cache, leaving them full of
+    clean lines (outside the timed region; HIP events on `stream` bracket f
+    alone). A read rather than a fill: written lines would still be draining
+    to HBM while f runs."""
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < EXTRA_WARM_S:
+        f()
+        torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in pairs:
+        flush.sum()
+        e0.record(stream)
+        f()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in pairs) / reps * 1e3
+
+
+def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
+    """Every configuration the scan is specified on, each as its own launch
+    (the library's default kernel choice; no tuning override): the tiny fp32
+    case, the Mamba-130M layer, the packed-sequence scan with resets, the
+    Mamba-2.8B layer (the step's scan) and the decode step. Each is timed
+    back to back after a warm-up (warm: the inputs of a small case stay in
+    the 256 MB last-level cache between launches) and with the caches flushed
+    before every launch (cold)."""
+    import torch
+    from selective_state_space_ss_amd.workloads import WORKLOADS, make_inputs
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for name in ("tiny_fp32", "mamba130m", "packed_reset", "mamba2p8b"):
+        w = WORKLOADS[name]
+        if name == "mamba2p8b":
+            d = P
+        else:
+            d = {k: (None if v is None else v.cuda()) for k, v in make_inputs(w).items()}
+        y = torch.empty_like(d["x"])
+        h = torch.empty(w.batch, w.channels, w.state_dim, dtype=torch.float32, device="cuda")
+        f = lambda d=d, y=y, h=h: ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                                                 dt_bias=d["dt_bias"], h0=d["h0"], reset=d["reset"], y=y,
+                                                 h_last=h)
+        warm = scan_roofline(w, time_launches(f, stream, reps), rates)
+        cold = scan_roofline(w, time_cold(f, stream, reps, flush), rates)
+        res[name] = {"shape": {"batch": w.batch, "channels": w.channels, "state_dim": w.state_dim,
+                               "seq": w.seqlen, "io": w.io_dtype, "gate": w.gate, "h0": w.h0 is not None,
+                               "reset": w.reset_mean_doc is not None},
+                     "warm": warm, "cold": cold}
+        del d, y, h
+    state = Dd["state"].clone()
+    yd = torch.empty_like(Dd["x"])
+    fd = lambda: ss.ss_state_update(state, Dd["x"], Dd["dt"], Dd["A"], Dd["B"], Dd["C"], D=Dd["D"], z=Dd["z"],
+                                    dt_bias=Dd["dt_bias"], y=yd)
+    res["decode"] = {"shape": {"batch": wd.batch, "channels": wd.channels, "state_dim": wd.state_dim,
+                               "io": wd.io_dtype, "gate": wd.gate},
+                     "warm": decode_roofline(wd, time_launches(fd, stream, reps)),
+                     "cold": decode_roofline(wd, time_cold(fd, stream, reps, flush))}
+    del flush, state
+    return res
+
+
+def probe_live():
+    """The two pure issue-rate kernels, run in this process: a cross-check of
+    the committed rates on the box the bench runs on."""
+    import ctypes
+    from selective_state_space_ss_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.ssprobe_issue.restype = ctypes.c_int
+    lib.ssprobe_issue.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_double)] * 2
+    lanes = PROBE_BLOCKS * PROBE_THREADS * PROBE_ITERS
+    out = {}
+    for key, ne, nf in (("fma_lane_ops_per_s", 0, 16), ("exp2_lane_ops_per_s", 16, 0)):
+        ms, mhz = ctypes.c_double(), ctypes.c_double()
+        if lib.ssprobe_issue(ne, nf, PROBE_ITERS, PROBE_BLOCKS, ctypes.byref(ms), ctypes.byref(mhz)) != 0:
+            return None
+        out[key] = lanes * (ne + nf) / (ms.value * 1e-3)
+        out["clock_mhz"] = round(mhz.value, 1)
+    return out
+
+
 COPY_CEILING_BYTES = 1 << 30   # each way
 
 
@@ -350,6 +553,12 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.probe_issue:
+        r = measure_issue_rates()
+        with open(args.probe_issue, "w") as f:
+            json.dump(r, f, indent=1)
+        print(json.dumps(r), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the scan would shard over "
@@ -420,8 +629,10 @@ def main():
 
     bytes_p, bytes_d = algorithmic_bytes(wp), algorithmic_bytes(wd)
     ct_p, ct_d = wp.channel_tokens, wd.channel_tokens
-    flops = roofline_flops(wp)
-    achieved = flops / (scan_ms * 1e-3) / 1e12
+    rates = issue_rates()
+    scan_r = scan_roofline(wp, scan_ms * 1e3, rates)
+    dec_r = decode_roofline(wd, upd_ms * 1e3)
+    wk = scan_work(wp)
     out = {
         "metric": "selective-scan GB/s + channel-tokens/s at Mamba-2.8B layer shape; % roofline",
         "value": round((bytes_p + bytes_d) / (ms_step * 1e-3) / 1e9, 2),
@@ -444,27 +655,29 @@ def main():
             "parallelism": "single GPU",
         },
         "channel_tokens_per_s": round((ct_p + ct_d) / (ms_step * 1e-3), 1),
-        "kernels": {
-            "ss_scan_fwd": {"us": round(scan_ms * 1e3, 2), "GB_s": round(bytes_p / (scan_ms * 1e-3) / 1e9, 1),
-                            "channel_tokens_per_s": round(ct_p / (scan_ms * 1e-3), 1),
-                            "algorithmic_bytes": bytes_p},
-            "ss_state_update": {"us": round(upd_ms * 1e3, 2), "GB_s": round(bytes_d / (upd_ms * 1e-3) / 1e9, 1),
-                                "hbm_frac": round(bytes_d / (upd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                "algorithmic_bytes": bytes_d},
-        },
+        "kernels": {"ss_scan_fwd": scan_r, "ss_state_update": dec_r},
         "roofline": {
             "bound": "alu",
             "kernel": "ss_scan_fwd",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_FP32_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+            "achieved": round(wk["trans"] / (scan_ms * 1e-3) / 1e12, 4),
+            "peak": round(rates[1] / 1e12, 4),
+            "unit": "T transcendental lane-ops/s",
+            "frac": scan_r["frac"],
             "traffic": recorded_traffic(),
-            "flop_model": "FMA-equivalent per launch (FMA 2, mul 1, transcendental 8): "
-                          f"{flops:.4g}; HBM side: {bytes_p} algorithmic bytes = "
-                          f"{bytes_p / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f} of 8 TB/s",
+            "hbm_frac": scan_r["hbm_frac"],
+            "exp_frac": scan_r["exp_frac"],
+            "issue_frac": scan_r["issue_frac"],
+            "model": f"frac = max(HBM time, transcendental time) / kernel time. HBM: {bytes_p} algorithmic "
+                     f"bytes at {PEAK_HBM_GBS / 1e3:g} TB/s. Transcendental: {wk['trans']:.4g} per launch "
+                     f"(16 decay exp2 + softplus exp, log + gate exp, rcp per channel-token) at "
+                     f"{rates[1]:.4g} lane-ops/s, measured ({rates[2]}). issue_frac adds the "
+                     f"{wk['fma']:.4g} FMA-class operations the method needs at {rates[0]:.4g} lane-ops/s "
+                     f"(the same VALU issue slots).",
         },
     }
+    if not args.no_workloads:
+        out["workloads"] = measure_workloads(ss, stream, rates, P, wp, Dd, wd)
+    out["issue_probe_live"] = probe_live()
     if not args.no_extras:
         out["extras"] = {"ss_scan_fwd_states": measure_states(ss, P, wp, bytes_p, stream),
                          "ss_gated_scan": measure_gated(ss, stream),

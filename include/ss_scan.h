@@ -14,9 +14,12 @@
  * kernel calls the nnterp page names: the prompt scan
  * (x, dt, A, B, C, D=, z=, delta_bias=) and the single-token state update
  * (state, x, dt, A, B, C, D, z=, dt_bias=), and take the kernel's
- * channel-first layouts from the same page.
+ * channel-first layouts from the same page. Those two calls (and the scan
+ * that also returns states) take their tensors in an argument struct
+ * (ss_scan_args, ss_update_args) plus a stream; the other calls take flat
+ * argument lists.
  *
- * Conventions shared by both calls:
+ * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers to contiguous C-order arrays;
  *    the caller owns every buffer. The library allocates nothing and keeps no
  *    state between calls; calls are thread-safe.
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 6
+#define SS_ABI_VERSION 7
 #define SS_MAX_STATE_DIM 64
 #define SS_MAX_GATED_DK 256
 #define SS_MAX_CONV_WIDTH 8
@@ -63,7 +66,7 @@ typedef enum {
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
 /*
- * Prompt / prefill scan over seqlen tokens.
+ * Prompt / prefill scan over seqlen tokens: the arguments of ss_scan_fwd.
  *
  *   x, dt, z, y : [batch, channels, seqlen]   io_dtype
  *   B, C        : [batch, state_dim, seqlen]  io_dtype (one group: shared by
@@ -77,6 +80,7 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  *                 first token of a packed document: the state is zeroed
  *                 before that token, i.e. its decay exp(dt_t*A) is replaced
  *                 by 0 ("s6_reset" post, Enforced Boundary Resetting).
+ *   dt_softplus : nonzero: dt <- softplus(dt + dt_bias); zero: dt + dt_bias
  *   y           : output [batch, channels, seqlen] io_dtype
  *   h_last      : output [batch, channels, state_dim] float32, the state
  *                 after the last token (what the next call or decode step
@@ -84,12 +88,53 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  *                 be the same pointer as h0. With seqlen == 0 it receives
  *                 the initial state.
  *
- * batch == 0 or channels == 0 is a no-op returning SS_OK.
+ * io_dtype holds an ss_dtype value (an int32_t field, so that a caller can
+ * pass any integer and get SS_ERR_DTYPE back for a bad one).
  */
-int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
-                const void* x, const void* dt, const float* A, const void* B, const void* C,
-                const float* D, const void* z, const float* dt_bias, const float* h0,
-                const uint8_t* reset, int dt_softplus, void* y, float* h_last, void* stream);
+typedef struct {
+  int64_t batch, channels, state_dim, seqlen;
+  int32_t io_dtype;
+  const void *x, *dt;
+  const void* z;
+  const void *B, *C;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* h0;
+  const uint8_t* reset;
+  int32_t dt_softplus;
+  void* y;
+  float* h_last;
+} ss_scan_args;
+
+/*
+ * The single-token decode update's arguments (ss_state_update).
+ *
+ *   state       : [batch, channels, state_dim] float32, read and written
+ *   x, dt, z, y : [batch, channels]           io_dtype (z NULL = no gate)
+ *   B, C        : [batch, state_dim]          io_dtype
+ *   A           : [channels, state_dim]       float32
+ *   D, dt_bias  : [channels]                  float32, NULL reads as zeros
+ *   dt_softplus : as in ss_scan_args
+ */
+typedef struct {
+  int64_t batch, channels, state_dim;
+  int32_t io_dtype;
+  float* state;
+  const void *x, *dt, *z;
+  const void *B, *C;
+  const float *A, *D, *dt_bias;
+  int32_t dt_softplus;
+  void* y;
+} ss_update_args;
+
+/*
+ * Prompt scan (nnterp "selective_scan" page: the scan call
+ * (x, dt, A, B, C, D=, z=, delta_bias=) with its channel-first layouts).
+ * args must not be NULL (SS_ERR_NULL). batch == 0 or channels == 0 is a
+ * no-op returning SS_OK.
+ */
+ss_status ss_scan_fwd(const ss_scan_args* args, void* stream);
 
 /*
  * The prompt scan of ss_scan_fwd that also returns states of the recurrence
@@ -112,29 +157,16 @@ int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seql
  * states are 2 * state_dim times the size of a bf16 y), so that form is bound
  * by HBM bandwidth; the single-step form costs about what ss_scan_fwd does.
  */
-int ss_scan_fwd_states(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
-                       const void* x, const void* dt, const float* A, const void* B, const void* C,
-                       const float* D, const void* z, const float* dt_bias, const float* h0,
-                       const uint8_t* reset, int dt_softplus, void* y, float* h_last, float* states,
-                       int64_t time_step, void* stream);
+ss_status ss_scan_fwd_states(const ss_scan_args* args, float* states, int64_t time_step, void* stream);
 
 /*
  * Single-token decode update of a cached state, in place (nnterp
- * "selective_scan" page: the state-update call on one token; the updated
- * state is what the cache receives and y reads it).
- *
- *   state       : [batch, channels, state_dim] float32, read and written
- *   x, dt, z, y : [batch, channels]           io_dtype (z NULL = no gate)
- *   B, C        : [batch, state_dim]          io_dtype
- *   A           : [channels, state_dim]       float32
- *   D, dt_bias  : [channels]                  float32, NULL reads as zeros
- *
- * batch == 0 or channels == 0 is a no-op returning SS_OK.
+ * "selective_scan" page: the state-update call
+ * (state, x, dt, A, B, C, D, z=, dt_bias=) on one token; the updated state
+ * is what the cache receives and y reads it). args must not be NULL
+ * (SS_ERR_NULL). batch == 0 or channels == 0 is a no-op returning SS_OK.
  */
-int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_dtype, float* state,
-                    const void* x, const void* dt, const float* A, const void* B, const void* C,
-                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y,
-                    void* stream);
+ss_status ss_state_update(const ss_update_args* args, void* stream);
 
 /*
  * Scalar-gated state scan ("Mamba 2 Gated State Scan" problem page,

@@ -84,10 +84,13 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+MAX_DEFAULT_THREADS = 16   # a one-GPU share of the host's cores
+
+
 def _threads(threads: Optional[int]) -> int:
     if threads is not None:
         return max(1, int(threads))
-    return max(1, len(os.sched_getaffinity(0)))
+    return max(1, min(MAX_DEFAULT_THREADS, len(os.sched_getaffinity(0))))
 
 
 def _split_rows(rows: int, parts: int):

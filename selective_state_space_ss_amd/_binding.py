@@ -16,6 +16,25 @@ MAX_STATE_DIM = 64
 _lib = None
 
 
+class ScanArgs(ctypes.Structure):
+    """ss_scan_args of ss_scan.h (same field order and types)."""
+    _fields_ = [("batch", ctypes.c_int64), ("channels", ctypes.c_int64), ("state_dim", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("x", ctypes.c_void_p),
+                ("dt", ctypes.c_void_p), ("z", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("h0", ctypes.c_void_p), ("reset", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("y", ctypes.c_void_p), ("h_last", ctypes.c_void_p)]
+
+
+class UpdateArgs(ctypes.Structure):
+    """ss_update_args of ss_scan.h (same field order and types)."""
+    _fields_ = [("batch", ctypes.c_int64), ("channels", ctypes.c_int64), ("state_dim", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("state", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("dt", ctypes.c_void_p), ("z", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("dt_softplus", ctypes.c_int32), ("y", ctypes.c_void_p)]
+
+
 class SSError(RuntimeError):
     """A non-zero ss_status returned by the library."""
 
@@ -41,9 +60,9 @@ def load_library() -> ctypes.CDLL:
     lib = ctypes.CDLL(_LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.ss_scan_fwd.restype = i32
-    lib.ss_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp]
+    lib.ss_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), vp]
     lib.ss_scan_fwd_states.restype = i32
-    lib.ss_scan_fwd_states.argtypes = [i64, i64, i64, i64, i32] + [vp] * 10 + [i32, vp, vp, vp, i64, vp]
+    lib.ss_scan_fwd_states.argtypes = [ctypes.POINTER(ScanArgs), vp, i64, vp]
     lib.ss_gated_scan.restype = i32
     lib.ss_gated_scan.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 7 + [vp]
     lib.ss_effective_attention.restype = i32
@@ -53,7 +72,7 @@ def load_library() -> ctypes.CDLL:
     lib.ss_dt_proj.restype = i32
     lib.ss_dt_proj.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp]
     lib.ss_state_update.restype = i32
-    lib.ss_state_update.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [i32, vp, vp]
+    lib.ss_state_update.argtypes = [ctypes.POINTER(UpdateArgs), vp]
     lib.ss_status_str.restype = ctypes.c_char_p
     lib.ss_status_str.argtypes = [i32]
     lib.ss_abi_version.restype = i32
@@ -114,7 +133,7 @@ def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=Non
     """
     y, h_last, args, dev = _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
                                       return_last_state)
-    rc = load_library().ss_scan_fwd(*args, _stream_handle(dev, stream))
+    rc = load_library().ss_scan_fwd(ctypes.byref(args), _stream_handle(dev, stream))
     if rc != SS_OK:
         raise SSError(rc, "ss_scan_fwd")
     return y, h_last
@@ -140,7 +159,7 @@ def ss_scan_fwd_states(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, re
         states = torch.empty(shape, dtype=torch.float32, device=dev)
     else:
         _check(states, "states", shape, torch.float32, dev)
-    rc = load_library().ss_scan_fwd_states(*args, _ptr(states), ts, _stream_handle(dev, stream))
+    rc = load_library().ss_scan_fwd_states(ctypes.byref(args), _ptr(states), ts, _stream_handle(dev, stream))
     if rc != SS_OK:
         raise SSError(rc, "ss_scan_fwd_states")
     return y, h_last, states
@@ -148,7 +167,7 @@ def ss_scan_fwd_states(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, re
 
 def _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last, return_last_state):
     """Check the scan's tensors, allocate missing outputs; returns y, h_last,
-    the C arguments up to h_last, and the device."""
+    the ss_scan_args struct, and the device."""
     import torch
     if x.dim() != 3:
         raise ValueError("x must be [batch, channels, seq]")
@@ -186,8 +205,9 @@ def _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
         h_last = torch.empty((batch, channels, N), dtype=torch.float32, device=dev)
     elif h_last is not None:
         _check(h_last, "h_last", (batch, channels, N), torch.float32, dev)
-    args = (batch, channels, N, L, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-            _ptr(dt_bias), _ptr(h0), _ptr(reset), int(bool(dt_softplus)), _ptr(y), _ptr(h_last))
+    args = ScanArgs(batch=batch, channels=channels, state_dim=N, seqlen=L, io_dtype=code, x=_ptr(x), dt=_ptr(dt),
+                    z=_ptr(z), B=_ptr(B), C=_ptr(C), A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias), h0=_ptr(h0),
+                    reset=_ptr(reset), dt_softplus=int(bool(dt_softplus)), y=_ptr(y), h_last=_ptr(h_last))
     return y, h_last, args, dev
 
 
@@ -389,9 +409,10 @@ def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_soft
     else:
         _check(y, "y", (batch, channels), io, dev)
     lib = load_library()
-    rc = lib.ss_state_update(batch, channels, N, code, _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                             _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y),
-                             _stream_handle(dev, stream))
+    args = UpdateArgs(batch=batch, channels=channels, state_dim=N, io_dtype=code, state=_ptr(state), x=_ptr(x),
+                      dt=_ptr(dt), z=_ptr(z), B=_ptr(B), C=_ptr(C), A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias),
+                      dt_softplus=int(bool(dt_softplus)), y=_ptr(y))
+    rc = lib.ss_state_update(ctypes.byref(args), _stream_handle(dev, stream))
     if rc != SS_OK:
         raise SSError(rc, "ss_state_update")
     return y

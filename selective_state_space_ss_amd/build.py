@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssscan.so")
+# measurement support for bench.py (issue-rate probe), kept out of the scan's library
+PROBE_LIB = os.path.join(PKG, "libssprobe.so")
+PROBE_SOURCES = ["probe_issue.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
@@ -70,11 +73,13 @@ def build(verbose: bool = False) -> str:
             print(out)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp%d" % os.getpid()
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[objs[n] for n in names]])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -30,10 +30,15 @@ int device_cus() {
 // 316.5 against 332.7 us (354.9 against 370.5 with a gate). At seq 4096 the
 // two were even, and at 2048 K = 16 was faster (90.1 against 92.5 us). At
 // 8 x 5120 channels x 2048 (2560 blocks) K = 16 was far faster (371.8 against
-// 415.2 us). SS_SCAN_TOKENS_PER_LANE=16|32 (read at every call) overrides the
-// choice.
+// 415.2 us). SS_SCAN_TOKENS_PER_LANE=16 or =32 (read at every call) overrides
+// the choice; any other value leaves it to the rule.
 int pick_k(const ScanParams& p) {
-  if (const char* e = std::getenv("SS_SCAN_TOKENS_PER_LANE")) return std::atoi(e) == 32 ? 32 : 16;
+  if (const char* e = std::getenv("SS_SCAN_TOKENS_PER_LANE")) {
+    const std::string v(e);
+    if (v == "16") return 16;
+    if (v == "32") return 32;
+    // anything else: the shape rule below
+  }
   const int64_t blocks = p.batch * ((p.channels + 15) / 16);
   return (p.reset != nullptr && p.L >= 8192 && blocks <= 2 * static_cast<int64_t>(device_cus())) ? 32 : 16;
 }

@@ -1,17 +1,17 @@
 // Prompt / prefill selective scan for gfx950, row-parallel form: every lane
 // owns one channel row and walks the whole sequence token by token, for the
-// four state coordinates of its wave.
+// two state coordinates of its wave.
 //
 // This form applies the recurrence of the nnterp "selective_scan" page, class
 // docstring, token by token, with no fold and no cross-lane scan: one exp and
 // four FMA-class operations per token and state coordinate (dt*A, dt*x*B,
 // h = a h + b, y += C h), against five for the chunked scan. It has
-// batch*channels*N/4 lanes of parallelism, so it serves shapes with many rows
+// batch*channels*N/2 lanes of parallelism, so it serves shapes with many rows
 // (the launcher decides).
 //
-// Layout. A block is 64 channel rows of one batch row times 4 waves; in the
+// Layout. A block is 64 channel rows of one batch row times 8 waves; in the
 // walk, lane r of every wave is row r and wave g holds state coordinates
-// 4g..4g+3. A wave's coordinates are the same in every lane, so B[b, n, t]
+// 2g, 2g+1. A wave's coordinates are the same in every lane, so B[b, n, t]
 // and C[b, n, t] are wave-uniform: they come through scalar loads into SGPRs
 // (widened there from bf16) and feed the vector instructions directly, and
 // so do the reset flags, which depend on (b, t) only. Tokens go in tiles of
@@ -19,13 +19,13 @@
 // SGPRs either way):
 //   1. the block computes dt = softplus(dt + dt_bias) and dt*x for its
 //      64 rows x kT tokens and publishes them in LDS; here thread i owns row
-//      i/4 and the token pairs i%4 + 4k, so 4 neighbouring lanes read 4
+//      i/8 and the token pairs i%8 + 8k, so 8 neighbouring lanes read 8
 //      contiguous pairs of a row;
-//   2. every wave walks the tile for its four coordinates and keeps the
+//   2. every wave walks the tile for its two coordinates and keeps the
 //      partial y_t = sum over its coordinates of C[n,t] h_t;
-//   3. the partials go to LDS; thread i sums the 4 waves' partials of its
+//   3. the partials go to LDS; thread i sums the 8 waves' partials of its
 //      (row, token pairs), applies D*x and silu(z), and stores y.
-// Two barriers per tile, each over 4 waves. The next tile's x, dt, z are
+// Two barriers per tile, each over 8 waves. The next tile's x, dt, z are
 // loaded one tile ahead, and its B, C and flags are loaded right after the
 // second barrier, so their latency hides behind phase 3 and the next phase 1.
 // Coordinates n >= N take no part (B = C = 0, A = 0: the state stays 0); a

@@ -58,53 +58,42 @@ int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, void* st
 
 extern "C" {
 
-int ss_scan_fwd(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype, const void* x,
-                const void* dt, const float* A, const void* B, const void* C, const float* D, const void* z,
-                const float* dt_bias, const float* h0, const uint8_t* reset, int dt_softplus, void* y,
-                float* h_last, void* stream) {
-  const ss::ScanArgs a{batch, channels, state_dim, seqlen, io_dtype, x,     dt,          A,
-                       B,     C,        D,         z,      dt_bias,  h0,    reset, dt_softplus, y, h_last};
-  return scan_entry(a, nullptr, -1, stream);
+ss_status ss_scan_fwd(const ss_scan_args* args, void* stream) {
+  if (!args) return SS_ERR_NULL;
+  return static_cast<ss_status>(scan_entry(*args, nullptr, -1, stream));
 }
 
-int ss_scan_fwd_states(int64_t batch, int64_t channels, int64_t state_dim, int64_t seqlen, int io_dtype,
-                       const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                       const void* z, const float* dt_bias, const float* h0, const uint8_t* reset, int dt_softplus,
-                       void* y, float* h_last, float* states, int64_t time_step, void* stream) {
-  const ss::ScanArgs a{batch, channels, state_dim, seqlen, io_dtype, x,     dt,          A,
-                       B,     C,        D,         z,      dt_bias,  h0,    reset, dt_softplus, y, h_last};
-  if (!states) return SS_ERR_NULL;
-  return scan_entry(a, states, time_step, stream);
+ss_status ss_scan_fwd_states(const ss_scan_args* args, float* states, int64_t time_step, void* stream) {
+  if (!args || !states) return SS_ERR_NULL;
+  return static_cast<ss_status>(scan_entry(*args, states, time_step, stream));
 }
 
-int ss_state_update(int64_t batch, int64_t channels, int64_t state_dim, int io_dtype, float* state, const void* x,
-                    const void* dt, const float* A, const void* B, const void* C, const float* D, const void* z,
-                    const float* dt_bias, int dt_softplus, void* y, void* stream) {
-  const ss::UpdateArgs a{batch, channels, state_dim, io_dtype, state, x,       dt,          A,
-                         B,     C,        D,         z,        dt_bias, dt_softplus, y};
+ss_status ss_state_update(const ss_update_args* args, void* stream) {
+  if (!args) return SS_ERR_NULL;
+  const ss_update_args& a = *args;
   bool noop = false;
   const ss_status st = ss::validate_update(a, &noop);
   if (st != SS_OK || noop) return st;
-  if (!ss::state_update_grid_ok(batch, channels, state_dim)) return SS_ERR_SHAPE;
+  if (!ss::state_update_grid_ok(a.batch, a.channels, a.state_dim)) return SS_ERR_SHAPE;
   ss::UpdateParams p{};
-  p.batch = batch;
-  p.channels = channels;
-  p.N = (int)state_dim;
-  p.dt_softplus = dt_softplus != 0;
-  const uintptr_t bc_align = io_dtype == SS_BF16 ? 8 : 16;
-  p.vec_ok = (state_dim == 16 || state_dim == 32 || state_dim == 64) && vec16(state) && vec16(A) && (reinterpret_cast<uintptr_t>(B) % bc_align) == 0 &&
-             (reinterpret_cast<uintptr_t>(C) % bc_align) == 0;
-  p.state = state;
-  p.x = x;
-  p.dt = dt;
-  p.z = z;
-  p.B = B;
-  p.C = C;
-  p.A = A;
-  p.D = D;
-  p.dt_bias = dt_bias;
-  p.y = y;
-  const hipError_t e = ss::launch_state_update(p, io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  p.batch = a.batch;
+  p.channels = a.channels;
+  p.N = (int)a.state_dim;
+  p.dt_softplus = a.dt_softplus != 0;
+  const uintptr_t bc_align = a.io_dtype == SS_BF16 ? 8 : 16;
+  p.vec_ok = (a.state_dim == 16 || a.state_dim == 32 || a.state_dim == 64) && vec16(a.state) && vec16(a.A) &&
+             (reinterpret_cast<uintptr_t>(a.B) % bc_align) == 0 && (reinterpret_cast<uintptr_t>(a.C) % bc_align) == 0;
+  p.state = a.state;
+  p.x = a.x;
+  p.dt = a.dt;
+  p.z = a.z;
+  p.B = a.B;
+  p.C = a.C;
+  p.A = a.A;
+  p.D = a.D;
+  p.dt_bias = a.dt_bias;
+  p.y = a.y;
+  const hipError_t e = ss::launch_state_update(p, a.io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 

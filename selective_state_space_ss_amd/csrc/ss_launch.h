@@ -70,8 +70,8 @@ hipError_t launch_scan_rows(const ScanParams& p, bool io_bf16, hipStream_t strea
 // receives [batch, channels, N, L] (p.time_step < 0) or the state after token
 // p.time_step, [batch, channels, N].
 hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t stream);
-// The row-parallel walk needs an even L and x, dt, z, y, B, C (and reset)
-// aligned to two elements.
+// The row-parallel walk needs L a multiple of 4, N <= 16, x, dt, z, y, B, C
+// aligned to two elements and reset to 4 bytes.
 bool scan_rows_supported(const ScanParams& p, bool io_bf16);
 hipError_t launch_state_update(const UpdateParams& p, bool io_bf16, hipStream_t stream);
 // The scalar-gated state scan (gated_scan.hip); io_bf16: element type of q, k, v, y.

@@ -30,22 +30,8 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 inline bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
 
-// Inputs of the prompt scan, in ABI order; see ss_scan_fwd in ss_scan.h.
-struct ScanArgs {
-  int64_t batch, channels, state_dim, seqlen;
-  int io_dtype;
-  const void *x, *dt;
-  const float* A;
-  const void *B, *C;
-  const float* D;
-  const void* z;
-  const float* dt_bias;
-  const float* h0;
-  const uint8_t* reset;
-  int dt_softplus;
-  void* y;
-  float* h_last;
-};
+// The prompt scan's arguments are the public struct (ss_scan_fwd in ss_scan.h).
+using ScanArgs = ss_scan_args;
 
 // SS_OK means "launch"; *noop set means "valid and nothing to do".
 inline ss_status validate_scan(const ScanArgs& a, bool* noop) {
@@ -97,18 +83,18 @@ inline ss_status validate_scan_states(const ScanArgs& a, const float* states, in
   if (time_step >= a.seqlen) return SS_ERR_SHAPE;
   if (!aligned(states, 4)) return SS_ERR_ALIGN;
   const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
-  int64_t rows, st, tok, tok_bytes, bc_bytes, a_bytes, rs_bytes, s_bytes;
-  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, a.state_dim, &st) ||
+  int64_t rows, st, st_bytes, tok, tok_bytes, bn, bc_bytes, cn, a_bytes, rs_bytes, s_bytes;
+  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, a.state_dim, &st) || !mul_ok(st, 4, &st_bytes) ||
       !mul_ok(st, time_step < 0 ? a.seqlen : 1, &s_bytes) || !mul_ok(s_bytes, 4, &s_bytes) ||
-      !mul_ok(rows, a.seqlen, &tok) || !mul_ok(tok, es, &tok_bytes) ||
-      !mul_ok(a.batch * a.state_dim, a.seqlen * es, &bc_bytes) || !mul_ok(a.channels * a.state_dim, 4, &a_bytes) ||
-      !mul_ok(a.batch, a.seqlen, &rs_bytes))
+      !mul_ok(rows, a.seqlen, &tok) || !mul_ok(tok, es, &tok_bytes) || !mul_ok(a.batch, a.state_dim, &bn) ||
+      !mul_ok(bn, a.seqlen, &bc_bytes) || !mul_ok(bc_bytes, es, &bc_bytes) ||
+      !mul_ok(a.channels, a.state_dim, &cn) || !mul_ok(cn, 4, &a_bytes) || !mul_ok(a.batch, a.seqlen, &rs_bytes))
     return SS_ERR_SHAPE;
   const Span s(states, s_bytes);
   const Span others[] = {Span(a.x, tok_bytes),      Span(a.dt, tok_bytes),           Span(a.z, tok_bytes),
                          Span(a.B, bc_bytes),       Span(a.C, bc_bytes),             Span(a.A, a_bytes),
-                         Span(a.D, a.channels * 4), Span(a.dt_bias, a.channels * 4), Span(a.h0, st * 4),
-                         Span(a.reset, rs_bytes),   Span(a.y, tok_bytes),            Span(a.h_last, st * 4)};
+                         Span(a.D, a.channels * 4), Span(a.dt_bias, a.channels * 4), Span(a.h0, st_bytes),
+                         Span(a.reset, rs_bytes),   Span(a.y, tok_bytes),            Span(a.h_last, st_bytes)};
   for (const Span& o : others)
     if (s.overlaps(o)) return SS_ERR_ALIAS;
   return SS_OK;
@@ -281,20 +267,8 @@ inline ss_status validate_proj(const ProjArgs& a, bool* noop) {
   return SS_OK;
 }
 
-// Inputs of the decode step, in ABI order; see ss_state_update in ss_scan.h.
-struct UpdateArgs {
-  int64_t batch, channels, state_dim;
-  int io_dtype;
-  float* state;
-  const void *x, *dt;
-  const float* A;
-  const void *B, *C;
-  const float* D;
-  const void* z;
-  const float* dt_bias;
-  int dt_softplus;
-  void* y;
-};
+// The decode step's arguments are the public struct (ss_state_update in ss_scan.h).
+using UpdateArgs = ss_update_args;
 
 inline ss_status validate_update(const UpdateArgs& a, bool* noop) {
   *noop = false;

@@ -8,7 +8,7 @@ import subprocess
 import pytest
 
 import selective_state_space_ss_amd as ss
-from selective_state_space_ss_amd._binding import load_library
+from selective_state_space_ss_amd._binding import ScanArgs, UpdateArgs, load_library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ss_scan.h")
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 6
+    assert ss.abi_version() == 7
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -56,14 +56,50 @@ def test_status_strings_and_version(lib):
 MB = 1 << 20
 
 
-def scan_call(lib, batch=2, channels=8, N=16, L=64, io=1, x=1 * MB, dt=2 * MB, A=3 * MB, B=4 * MB, C=5 * MB,
+def scan_args(batch=2, channels=8, N=16, L=64, io=1, x=1 * MB, dt=2 * MB, A=3 * MB, B=4 * MB, C=5 * MB,
               D=None, z=None, bias=None, h0=None, reset=None, y=6 * MB, h_last=None):
-    return lib.ss_scan_fwd(batch, channels, N, L, io, x, dt, A, B, C, D, z, bias, h0, reset, 1, y, h_last, None)
+    return ScanArgs(batch=batch, channels=channels, state_dim=N, seqlen=L, io_dtype=io, x=x, dt=dt, z=z, B=B, C=C,
+                    A=A, D=D, dt_bias=bias, h0=h0, reset=reset, dt_softplus=1, y=y, h_last=h_last)
+
+
+def scan_call(lib, **kw):
+    return lib.ss_scan_fwd(ctypes.byref(scan_args(**kw)), None)
 
 
 def upd_call(lib, batch=2, channels=8, N=16, io=1, state=1 * MB, x=2 * MB, dt=3 * MB, A=4 * MB, B=5 * MB, C=6 * MB,
              D=None, z=None, bias=None, y=7 * MB):
-    return lib.ss_state_update(batch, channels, N, io, state, x, dt, A, B, C, D, z, bias, 1, y, None)
+    a = UpdateArgs(batch=batch, channels=channels, state_dim=N, io_dtype=io, state=state, x=x, dt=dt, z=z, B=B, C=C,
+                   A=A, D=D, dt_bias=bias, dt_softplus=1, y=y)
+    return lib.ss_state_update(ctypes.byref(a), None)
+
+
+def test_null_argument_structs(lib):
+    assert lib.ss_scan_fwd(None, None) == NULL
+    assert lib.ss_scan_fwd_states(None, 8 * MB, -1, None) == NULL
+    assert lib.ss_state_update(None, None) == NULL
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes mirrors of ss_scan_args and ss_update_args have the C
+    compiler's size and field offsets."""
+    fields = {"ss_scan_args": ScanArgs, "ss_update_args": UpdateArgs}
+    body = []
+    for cname, py in fields.items():
+        body.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            body.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "ss_scan.h"\nint main(void){' + "".join(body) +
+                   "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
 
 
 def test_scan_validation(lib):
@@ -87,10 +123,8 @@ def test_scan_validation(lib):
     assert scan_call(lib, channels=0, x=None, dt=None, B=None, C=None, y=None) == OK
 
 
-def states_call(lib, batch=2, channels=8, N=16, L=64, io=1, x=1 * MB, dt=2 * MB, A=3 * MB, B=4 * MB, C=5 * MB,
-                y=6 * MB, h_last=None, states=8 * MB, time_step=-1):
-    return lib.ss_scan_fwd_states(batch, channels, N, L, io, x, dt, A, B, C, None, None, None, None, None, 1, y,
-                                  h_last, states, time_step, None)
+def states_call(lib, states=8 * MB, time_step=-1, **kw):
+    return lib.ss_scan_fwd_states(ctypes.byref(scan_args(**kw)), states, time_step, None)
 
 
 def test_scan_states_validation(lib):
@@ -205,8 +239,35 @@ def test_binding_requires_device_tensors():
 def test_validator_header_builds_standalone(tmp_path):
     """The validation header has no HIP dependency (host-only g++ build)."""
     src = tmp_path / "t.cpp"
-    src.write_text('#include "ss_validate.h"\nint main(){ss::ScanArgs a{}; bool n; return ss::validate_scan(a,&n)==SS_ERR_UNSUPPORTED?0:1;}\n')
+    src.write_text('#include "ss_validate.h"\nint main(){ss_scan_args a{}; bool n; return ss::validate_scan(a,&n)==SS_ERR_UNSUPPORTED?0:1;}\n')
     exe = tmp_path / "t"
     subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-I",
                     os.path.join(ROOT, "selective_state_space_ss_amd", "csrc"), str(src), "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def _device_visible() -> bool:
+    if os.path.exists("/dev/kfd"):
+        return True
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_launch_without_a_device_returns_hip_error(lib):
+    """With no GPU present, valid calls get past validation and the failed
+    launch comes back as SS_ERR_HIP rather than a crash. The pointers here are
+    fake, so the test never runs where a GPU is visible."""
+    if _device_visible():
+        pytest.skip("a GPU is visible: this test launches with fake pointers")
+    assert scan_call(lib) == HIP
+    assert scan_call(lib, io=0, z=7 * MB, h0=8 * MB, h_last=9 * MB, reset=10 * MB) == HIP
+    assert states_call(lib) == HIP
+    assert states_call(lib, time_step=3) == HIP
+    assert upd_call(lib) == HIP
+    assert gated_call(lib) == HIP
+    assert attn_call(lib) == HIP
+    assert conv_call(lib) == HIP
+    assert proj_call(lib) == HIP

@@ -12,9 +12,12 @@ from tests.helpers import TOL, TOL_STATE, check_close, np64, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["chunked", "rows"])
+@pytest.fixture(params=["chunked", "chunked32", "rows"])
 def scan_kernel(request, monkeypatch):
-    monkeypatch.setenv("SS_SCAN_KERNEL", request.param)
+    """Both prompt-scan kernels, the chunked one at 16 and at 32 tokens per
+    lane (SS_SCAN_KERNEL and SS_SCAN_TOKENS_PER_LANE force one)."""
+    monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if request.param == "rows" else "chunked")
+    monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if request.param == "chunked32" else "16")
     return request.param
 
 

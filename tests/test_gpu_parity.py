@@ -52,21 +52,95 @@ def test_workload_tiny_fp32():
     compare_full(inp, what="tiny_fp32")
 
 
+# The oracle's results for the full-size workloads, computed once per module
+# and shared by every kernel variant that is compared with them.
+_FULL = {}
+
+
+def full_size_reference(name):
+    if name not in _FULL:
+        inp = make_inputs(name)
+        print(f"oracle over every row of {name}", flush=True)
+        yr, hr = oracle_scan_full(inp)
+        _FULL[name] = (inp, yr, hr)
+    return _FULL[name]
+
+
 @pytest.mark.parametrize("name", ["mamba130m", "mamba2p8b", "packed_reset"])
-def test_workload_full_size_sampled_rows(name, scan_kernel):
-    """The full-size launch (the benchmark's), checked on sampled rows."""
+def test_workload_full_size_every_element(name, scan_kernel):
+    """The full-size launch (the benchmark's), every element of y and h_last
+    against the oracle run over every row."""
     w = WORKLOADS[name]
     print(f"workload {name} full size, {scan_kernel} kernel", flush=True)
-    inp = make_inputs(name)
+    inp, yr, hr = full_size_reference(name)
     y, h = run_scan(inp)
-    rows = sample_rows(w.batch, w.channels, 40, seed=7)
-    yr, hr = oracle_scan_rows(inp, rows)
-    yg = np.stack([np64(y[b, c]) for b, c in rows])
-    hg = np.stack([np64(h[b, c]) for b, c in rows])
     rtol, atol = TOL[w.io_dtype]
-    check_close(yg, yr, rtol, atol, f"y {name}")
-    check_close(hg, hr, *TOL_STATE, f"h_last {name}")
-    assert torch.isfinite(y.float()).all() and torch.isfinite(h).all()
+    check_close(np64(y), yr, rtol, atol, f"y {name}")
+    check_close(np64(h), hr, *TOL_STATE, f"h_last {name}")
+
+
+def test_packed_reset_default_kernel_choice(monkeypatch):
+    """The library's own choice of tokens per lane (no override): with a reset
+    mask and a long sequence on few channels it takes 32 tokens per lane;
+    every element against the oracle."""
+    monkeypatch.delenv("SS_SCAN_TOKENS_PER_LANE", raising=False)
+    monkeypatch.delenv("SS_SCAN_KERNEL", raising=False)
+    print("default kernel choice: bf16 1 x 64 x 16 x 8192 with resets", flush=True)
+    inp = make_case(905, 1, 64, 16, 8192, "bf16", gate=True, h0=True, reset_mean_doc=512)
+    compare_full(inp, what="default choice 1x64x8192")
+    inp, yr, hr = full_size_reference("packed_reset")
+    y, h = run_scan(inp)
+    check_close(np64(y), yr, *TOL["bf16"], "y packed_reset default choice")
+    check_close(np64(h), hr, *TOL_STATE, "h_last packed_reset default choice")
+
+
+def _edge_mask(kind, batch, L):
+    """Deterministic reset masks on the kernels' lane and chunk edges (16 or
+    32 tokens per lane, 16 lanes per chunk)."""
+    m = torch.zeros(batch, L, dtype=torch.uint8)
+    t = torch.arange(L)
+    if kind == "every_token":
+        m[:] = 1
+    elif kind == "lane16":
+        m[:, t % 16 == 0] = 1
+    elif kind == "chunk256":
+        m[:, t % 256 == 0] = 1
+    elif kind == "lane32":
+        m[:, t % 32 == 0] = 1
+    elif kind == "chunk512":
+        m[:, t % 512 == 0] = 1
+    elif kind == "straddle":
+        for e in (256, 512, 768, 1024):      # two adjacent resets across each chunk edge
+            if e < L:
+                m[:, e - 1:e + 1] = 1
+        m[:, 15:17] = 1                       # and across a lane edge
+    elif kind == "first_only":
+        m[:, 0] = 1
+    elif kind == "last_only":
+        m[:, L - 1] = 1
+    elif kind == "lane_ends":
+        m[:, (t % 16 == 15) | (t % 32 == 31)] = 1
+    else:
+        raise ValueError(kind)
+    return m
+
+
+EDGE_KINDS = ["every_token", "lane16", "chunk256", "lane32", "chunk512", "straddle", "first_only", "last_only",
+              "lane_ends"]
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", EDGE_KINDS)
+def test_reset_edges(kind, io, scan_kernel):
+    """Resets placed on every token, on lane and chunk boundaries, in adjacent
+    pairs straddling them, and with an initial state ("s6_reset" post,
+    Enforced Boundary Resetting: the state is zeroed before a document's
+    first token; a reset at t = 0 discards h0)."""
+    print(f"reset edges {kind} io={io} kernel={scan_kernel}", flush=True)
+    L = 1100
+    inp = make_case(920 + EDGE_KINDS.index(kind), 2, 19, 16, L, io, gate=True, h0=True)
+    inp["reset"] = _edge_mask(kind, 2, L)
+    compare_full(inp, what=f"reset {kind} {io}")
 
 
 @pytest.mark.parametrize("N", [32, 64])
