@@ -133,6 +133,9 @@ def parse():
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes into " + TRAFFIC_FILE)
+    ap.add_argument("--summarize-trace", metavar="KT_DIR",
+                    help="print a markdown table of a rocprofv3 --kernel-trace directory, one row per kernel and "
+                         "launch shape (grid x block), and exit")
     ap.add_argument("--probe-issue", metavar="OUT_JSON",
                     help="run the fp32 FMA / transcendental issue-rate probe, write its JSON to OUT_JSON, exit")
     return ap.parse_args()
@@ -178,9 +181,26 @@ def measure_issue_rates():
             te, tf = lanes * ne / exp_rate, lanes * nf / fma_rate
             mixes.append({"exp2_per_iter": ne, "fma_per_iter": nf, "s": t, "no_overlap_s": te + tf,
                           "full_overlap_s": max(te, tf), "measured_over_no_overlap": round(t / (te + tf), 4)})
+    # dependent chains at 1 and 2 waves per SIMD (256 and 512 blocks of 4
+    # waves): how many independent chains a wave needs to keep its SIMD busy
+    chains = []
+    for blocks in (256, 512):
+        for ne, nf in ((0, 1), (0, 2), (0, 4), (0, 8), (1, 0), (2, 0), (4, 0), (8, 0)):
+            cms, cmhz = ctypes.c_double(), ctypes.c_double()
+            iters = PROBE_ITERS // 4
+            if lib.ssprobe_issue(ne, nf, iters, blocks, ctypes.byref(cms), ctypes.byref(cmhz)) != 0:
+                raise RuntimeError(f"ssprobe_issue({ne}, {nf}) at {blocks} blocks failed")
+            waves_per_simd = blocks * PROBE_THREADS // 64 // (4 * 256)
+            kclk = cms.value * 1e-3 * cmhz.value * 1e6
+            per_instr = kclk / (iters * (ne + nf) * waves_per_simd)   # SIMD clocks per wave instruction
+            chains.append({"waves_per_simd": waves_per_simd, "exp2_chains": ne, "fma_chains": nf,
+                           "simd_clocks_per_instruction": round(per_instr, 2)})
+            print(f"chains exp2 x{ne} fma x{nf} at {waves_per_simd} waves/SIMD: {per_instr:.2f} clocks/instr",
+                  file=sys.stderr, flush=True)
     return {
         "probe": "libssprobe.so ssprobe_issue: %d blocks x %d threads x %d iterations per kernel"
                  % (PROBE_BLOCKS, PROBE_THREADS, PROBE_ITERS),
+        "dependent_chains": chains,
         "fma_lane_ops_per_s": fma_rate,
         "exp2_lane_ops_per_s": exp_rate,
         "clock_mhz_measured": mhz,
@@ -243,6 +263,32 @@ def summarize_traffic(fetch_dir, write_dir):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def summarize_trace(kt_dir):
+    """One row per (kernel, grid, block) of a rocprofv3 kernel-trace CSV: calls,
+    average / median / min / max duration. Launches of one kernel instance at
+    different shapes (say two workloads sharing a template instance) get rows
+    of their own."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True)
+    assert files, f"no *kernel_trace.csv under {kt_dir}"
+    groups = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+                   int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in groups.values())
+    print("| kernel | grid (work-items) | block | calls | average ns | median ns | min ns | max ns | share |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for (name, grid, block), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0].replace("void ", "") if "(anonymous namespace)" not in name else \
+            name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+        print(f"| `{short}` | {grid} | {block} | {len(d)} | {sum(d) / len(d):.0f} | {statistics.median(d):.0f} | "
+              f"{min(d)} | {max(d)} | {100.0 * sum(d) / total:.2f} % |")
 
 
 def recorded_traffic():
@@ -553,6 +599,9 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     if args.probe_issue:
         r = measure_issue_rates()

@@ -24,7 +24,7 @@ PROBE_LIB = os.path.join(PKG, "libssprobe.so")
 PROBE_SOURCES = ["probe_issue.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
+SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_fwd_reset.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
@@ -32,17 +32,20 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-# Per-source additions. The chunked prompt scan and its states variants are
-# scheduled with LLVM's iterative-ILP machine scheduler. On MI355X it measured
-# 342 against 346.5 us at batch 8 x 5120 channels x 2048 tokens, 85.7 against
-# 89.0 us at 4 x 1536 x 2048 (no change with resets), and 360 against 374 us
-# (one selected state) and 1445 against 1456 us (every state) at the first
-# shape, with identical results. The other files keep the default: with it
-# the producers, the attention and the decode step measured no change, and
-# this toolchain's compiler aborts on gated_scan.hip (max-ilp made that
-# kernel 14 % slower).
+# Per-source additions. The chunked prompt scan's instances with a reset mask
+# (scan_fwd_reset.hip) and the states variants are scheduled with LLVM's
+# iterative-ILP machine scheduler; the plain scan without resets
+# (scan_fwd.hip) keeps the default one. Measured on MI355X (same-box A/B, the
+# current kernels): packed sequences with resets 312.6 us with iterative-ILP
+# against 318.1 us with the default scheduler (4 x 2048 x 8192); without
+# resets 333.7 against 330.2 us (8 x 5120 x 2048) and 84.7 against 83.7 us
+# (4 x 1536 x 2048). The states variants measured 360 against 374 us (one
+# selected state) and 1445 against 1456 us (every state) with it. The other
+# files keep the default: with it the producers, the attention and the decode
+# step measured no change, and this toolchain's compiler aborts on
+# gated_scan.hip (max-ilp made that kernel 14 % slower).
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-SOURCE_FLAGS = {"scan_fwd.hip": _ILP, "scan_states.hip": _ILP}
+SOURCE_FLAGS = {"scan_fwd_reset.hip": _ILP, "scan_states.hip": _ILP}
 
 
 def hipcc() -> str:

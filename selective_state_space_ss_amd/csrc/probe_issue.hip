@@ -68,6 +68,9 @@ const Entry kEntries[] = {
     {2, 8, issue_probe_kernel<2, 8>},  {4, 8, issue_probe_kernel<4, 8>},  {8, 8, issue_probe_kernel<8, 8>},
     {1, 4, issue_probe_kernel<1, 4>},  {1, 5, issue_probe_kernel<1, 5>},  {4, 4, issue_probe_kernel<4, 4>},
     {0, 16, issue_probe_kernel<0, 16>}, {16, 0, issue_probe_kernel<16, 0>},
+    // few chains: with few waves per SIMD these expose the dependent-issue latency
+    {0, 1, issue_probe_kernel<0, 1>},  {0, 2, issue_probe_kernel<0, 2>},  {0, 4, issue_probe_kernel<0, 4>},
+    {1, 0, issue_probe_kernel<1, 0>},  {2, 0, issue_probe_kernel<2, 0>},  {4, 0, issue_probe_kernel<4, 0>},
 };
 
 }  // namespace

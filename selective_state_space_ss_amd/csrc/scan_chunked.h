@@ -29,9 +29,12 @@
 // is the final state, written to h_last.
 //
 // The kernel is bound by VALU issue (one exp and five FMA-class operations
-// per token and state coordinate), so its shape is chosen for occupancy: the
-// state coordinates run in a rolled loop that keeps one coordinate's K-token
-// arrays live, and the per-row constants and the carried state sit in LDS.
+// per token and state coordinate, next to nothing else: on gfx950 an exp2
+// occupies the issue port for two FMA slots and overlaps nothing), so every
+// instruction outside that core is one too many. The state coordinates run
+// one after another (unrolled, so every LDS offset is an immediate), keeping
+// one coordinate's K-token arrays live; the per-row constants and the
+// carried state sit in LDS.
 #pragma once
 
 #include "ss_device.h"
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
   __shared__ float sC[NG][kRowLanes][KP];
   __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
   __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
+  __shared__ float sZero[NMAX];              // what lanes 1..15 read in place of the carry
   // kAllStates: one coordinate's states of the chunk per row, each lane's K
   // tokens padded to KP, re-read in token order for coalesced stores
   __shared__ __align__(16) float sSt[STATES == kAllStates ? S::kChan : 1][STATES == kAllStates ? kRowLanes * KP : 1];
@@ -118,6 +122,12 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     sA2[slot + n] = n < N ? p.A[c * N + n] * kLog2e : 0.0f;
     sCarry[slot + n] = (n < N && p.h0) ? p.h0[(b * p.channels + c) * N + n] : 0.0f;
   }
+  for (int n = tid; n < NMAX; n += S::kThreads) sZero[n] = 0.0f;
+  // The carried state enters a chunk at lane 0 of each row; the other lanes
+  // read zeros in its place, so the first fold step needs no select. sZero is
+  // only ever read after the first chunk's staging barrier.
+  const float* __restrict__ carry_src = tl == 0 ? &sCarry[slot] : sZero;
+  const bool carry_writer = tl == kRowLanes - 1;  // lane 15 ends the chunk
   const float Dc = p.D ? p.D[c] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[c] : 0.0f;
 
@@ -127,16 +137,18 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     const int64_t tb = t0 + tl * K;  // this lane's first token
     const bool full = p.vec_ok && (t0 + T <= L);
 
-    // 1. this lane's tokens of x and dt, and z (raw; it is needed only after
-    // the state loop, and loading it here keeps its latency out of the way)
+    // 1. this lane's tokens of x and dt. z is loaded after the state loop:
+    // held in registers across the loop it costs registers the loop needs
+    // (spills), and the other waves of the SIMD cover its latency. (Measured
+    // on MI355X at batch 8 x 5120 x 2048: 334.4 us, against 348.8 us with z
+    // held in registers and 348.1 us with z copied global -> LDS by
+    // global_load_lds at the chunk's start.)
     float xv[K], dv[K];
-    uint4 zraw[GATE ? K / VEC : 1];
     if (full) {
 #pragma unroll
       for (int v = 0; v < K / VEC; ++v) {
         load_vec16(xg + tb + v * VEC, xv + v * VEC);
         load_vec16(dg + tb + v * VEC, dv + v * VEC);
-        if constexpr (GATE) zraw[v] = *reinterpret_cast<const uint4*>(zg + tb + v * VEC);
       }
     } else {
 #pragma unroll
@@ -181,16 +193,15 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
           const int sl = tpos / K, sj = tpos - sl * K;
           float vb[VEC], vc[VEC];
           const int64_t g = (int64_t)n * L + t0 + tpos;
-          if (n >= N) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) vb[e] = vc[e] = 0.0f;
-          } else if (full) {
+          // (each branch stores its own values: with one shared set the
+          // compiler zero-fills it on the common path too)
+          if (full && n < N) {
             load_vec16(Bg + g, vb);
             load_vec16(Cg + g, vc);
           } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-              const bool in = t0 + tpos + e < L;
+              const bool in = n < N && t0 + tpos + e < L;
               vb[e] = in ? Io<IoT>::to_f32(Bg[g + e]) : 0.0f;
               vc[e] = in ? Io<IoT>::to_f32(Cg[g + e]) : 0.0f;
             }
@@ -209,14 +220,13 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     // 3. per-token step size, dt*x, skip term
     float dtv[K], dtx[K], yv[K], mj[RESET ? K : 1];
     float sdt = 0.0f, mlane = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) dtv[j] = dv[j] + bias;
     // (uniform branches, so that whole chunks run neither a select per
     // token for the softplus switch nor the bounds mask)
     if (p.dt_softplus) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) dtv[j] = softplus_f32(dv[j] + bias);
-    } else {
-#pragma unroll
-      for (int j = 0; j < K; ++j) dtv[j] = dv[j] + bias;
+      for (int j = 0; j < K; ++j) dtv[j] = softplus_f32(dtv[j]);
     }
     if (!full) {
 #pragma unroll
@@ -235,19 +245,20 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
       }
     }
 
-    // 4. the group's state coordinates, one per iteration. With kOneState,
-    // the lane whose tokens hold time_step keeps the state after it.
+    // 4. the group's state coordinates, one after another (unrolled: every
+    // LDS offset is an immediate). With kOneState, the lane whose tokens hold
+    // time_step keeps the state after it.
     int jsel = -1;
     if constexpr (STATES == kOneState) {
       const int64_t jd = p.time_step - tb;
       jsel = (jd >= 0 && jd < K) ? (int)jd : -1;
     }
     auto coords = [&](int grp) {
-#pragma unroll 1
+#pragma unroll
       for (int nl = 0; nl < NG; ++nl) {
         const int n = grp * NG + nl;
         const float a2n = sA2[slot + n];
-        const float carry = sCarry[slot + n];
+        const float carry_l = carry_src[n];
         float av[K], bv[K];
 #pragma unroll
         for (int j = 0; j < K; j += 4) {
@@ -260,14 +271,16 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
           av[j] = fast_exp2(e);
           bv[j] *= dtx[j];
         }
-        float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2n, mlane) : sdt * a2n);
-        // fold from a zero state; lane 0 starts from the carried state instead
-        float Bl = __builtin_fmaf(av[0], tl == 0 ? carry : 0.0f, bv[0]);
+        const float Al = fast_exp2(RESET ? __builtin_fmaf(sdt, a2n, mlane) : sdt * a2n);
+        // fold from a zero state; lane 0 starts from the carried state (the
+        // other lanes read a zero carry, so their first step is exactly b0)
+        const float f0 = __builtin_fmaf(av[0], carry_l, bv[0]);
+        float Bl = f0;
 #pragma unroll
         for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
-        row16_inclusive_scan(Al, Bl);                            // Bl: state after this lane's tokens
-        float h = dpp_or<kDppRowShr1>(carry, Bl);                // state before them
-        sCarry[slot + n] = dpp_or<kDppRowNewBcast15>(Bl, Bl);    // state after the chunk (in place)
+        float h = f0;
+        row16_scan_and_enter(Al, Bl, h, av[0]);  // Bl: state after this lane's tokens; h: after its first
+        if (carry_writer) sCarry[slot + n] = Bl;  // state after the chunk (in place)
         float hsel = 0.0f;  // kOneState: the state after the selected token
 #pragma unroll
         for (int j = 0; j < K; j += 4) {
@@ -276,7 +289,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
           float h4[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            h = __builtin_fmaf(av[j + i], h, bv[j + i]);
+            if (j + i > 0) h = __builtin_fmaf(av[j + i], h, bv[j + i]);
             yv[j + i] = __builtin_fmaf(cq[i], h, yv[j + i]);
             h4[i] = h;
             if constexpr (STATES == kOneState) hsel = j + i == jsel ? h : hsel;
@@ -288,6 +301,13 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
         if constexpr (STATES == kOneState) {
           if (jsel >= 0 && n < N && row_ok) p.states[(b * p.channels + c) * N + n] = hsel;
         }
+        // Pin this coordinate's walk here: y is only read after the loop, so
+        // without this the compiler sinks every coordinate's walk to the end
+        // (all their K-token arrays live at once, and spilled); and keep the
+        // scheduler from interleaving coordinates for the same reason.
+#pragma unroll
+        for (int j = 0; j < K; ++j) asm volatile("" : "+v"(yv[j]));
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (STATES == kAllStates) {
           // states [batch, channels, N, L]: the row's 16 K tokens of
           // coordinate n, read back in token order from this row's own LDS
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
       float zv[K];
       if (full) {
 #pragma unroll
-        for (int v = 0; v < K / VEC; ++v) unpack_vec16<IoT>(zraw[v], zv + v * VEC);
+        for (int v = 0; v < K / VEC; ++v) load_vec16(zg + tb + v * VEC, zv + v * VEC);
       } else {
 #pragma unroll
         for (int j = 0; j < K; ++j) zv[j] = tb + j < L ? Io<IoT>::to_f32(zg[tb + j]) : 0.0f;
@@ -366,7 +386,11 @@ hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
 // per-token registers leave room for 3, so those blocks have 4 waves. K = 32
 // halves the per-chunk scan overhead at 2 waves per SIMD.
 // SS_SCAN_TOKENS_PER_LANE=16|32 overrides the choice (a tuning knob).
-template <typename IoT, int K, int NMAX, int STATES>
+// RESETS: which instantiations one call site compiles: 0 = without a reset
+// mask, 1 = with one, 2 = both (picked at run time). The plain scan keeps the
+// two sets in separate files, each built with the machine scheduler that
+// measured faster for it.
+template <typename IoT, int K, int NMAX, int STATES, int RESETS>
 hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   const bool gate = p.z != nullptr, reset = p.reset != nullptr;
   // 8-wave blocks when 4 waves fit per SIMD (two blocks per CU), else 4-wave
@@ -375,24 +399,31 @@ hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   // 4-wave blocks keep three blocks per CU)
   constexpr int W = (min_waves_per_simd<IoT, K, false>() == 4 && STATES != kAllStates) ? 8 : 4;
   constexpr int WR = 4;
-  if (gate && reset) return launch_t<IoT, K, WR, NMAX, true, true, STATES>(p, stream);
-  if (gate) return launch_t<IoT, K, W, NMAX, true, false, STATES>(p, stream);
-  if (reset) return launch_t<IoT, K, WR, NMAX, false, true, STATES>(p, stream);
-  return launch_t<IoT, K, W, NMAX, false, false, STATES>(p, stream);
+  if constexpr (RESETS != 0) {
+    if (reset || RESETS == 1) {
+      if (gate) return launch_t<IoT, K, WR, NMAX, true, true, STATES>(p, stream);
+      return launch_t<IoT, K, WR, NMAX, false, true, STATES>(p, stream);
+    }
+  }
+  if constexpr (RESETS != 1) {
+    if (gate) return launch_t<IoT, K, W, NMAX, true, false, STATES>(p, stream);
+    return launch_t<IoT, K, W, NMAX, false, false, STATES>(p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // N_max instances: 4, 8, 16, 32, 64 (coordinates past N run as the identity).
 // K = 32 is instantiated up to 16 coordinates only; wider states take K = 16.
-template <typename IoT, int K, int STATES>
+template <typename IoT, int K, int STATES, int RESETS>
 hipError_t launch_n(const ScanParams& p, hipStream_t stream) {
-  if (p.N <= 4) return launch_flags<IoT, K, 4, STATES>(p, stream);
-  if (p.N <= 8) return launch_flags<IoT, K, 8, STATES>(p, stream);
-  if (p.N <= 16) return launch_flags<IoT, K, 16, STATES>(p, stream);
+  if (p.N <= 4) return launch_flags<IoT, K, 4, STATES, RESETS>(p, stream);
+  if (p.N <= 8) return launch_flags<IoT, K, 8, STATES, RESETS>(p, stream);
+  if (p.N <= 16) return launch_flags<IoT, K, 16, STATES, RESETS>(p, stream);
   if constexpr (K == 16) {
-    if (p.N <= 32) return launch_flags<IoT, K, 32, STATES>(p, stream);
-    return launch_flags<IoT, K, 64, STATES>(p, stream);
+    if (p.N <= 32) return launch_flags<IoT, K, 32, STATES, RESETS>(p, stream);
+    return launch_flags<IoT, K, 64, STATES, RESETS>(p, stream);
   } else {
-    return launch_n<IoT, 16, STATES>(p, stream);
+    return launch_n<IoT, 16, STATES, RESETS>(p, stream);
   }
 }
 

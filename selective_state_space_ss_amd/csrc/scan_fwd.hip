@@ -1,5 +1,7 @@
 // Prompt / prefill selective scan for gfx950: launch of the plain scan (the
 // kernels are in scan_chunked.h and scan_rows.hip) and the choice between them.
+// This file instantiates the chunked kernel without a reset mask; the
+// instances with one are in scan_fwd_reset.hip.
 #include "scan_chunked.h"
 
 #include <atomic>
@@ -60,9 +62,10 @@ int pick_kernel(const ScanParams& p, bool io_bf16) {
 hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream) {
   if (pick_kernel(p, io_bf16) == 1) return launch_scan_rows(p, io_bf16, stream);
   const int K = pick_k(p);
+  if (p.reset) return launch_scan_fwd_reset(p, io_bf16, K, stream);
   if (io_bf16)
-    return K == 32 ? launch_n<bf16_t, 32, kNoStates>(p, stream) : launch_n<bf16_t, 16, kNoStates>(p, stream);
-  return K == 32 ? launch_n<float, 32, kNoStates>(p, stream) : launch_n<float, 16, kNoStates>(p, stream);
+    return K == 32 ? launch_n<bf16_t, 32, kNoStates, 0>(p, stream) : launch_n<bf16_t, 16, kNoStates, 0>(p, stream);
+  return K == 32 ? launch_n<float, 32, kNoStates, 0>(p, stream) : launch_n<float, 16, kNoStates, 0>(p, stream);
 }
 
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels) {

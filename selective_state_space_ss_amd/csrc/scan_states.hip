@@ -14,8 +14,8 @@ namespace ss {
 hipError_t launch_scan_states(const ScanParams& p, bool io_bf16, hipStream_t stream) {
   const bool all = p.time_step < 0;
   if (io_bf16)
-    return all ? launch_n<bf16_t, 16, kAllStates>(p, stream) : launch_n<bf16_t, 16, kOneState>(p, stream);
-  return all ? launch_n<float, 16, kAllStates>(p, stream) : launch_n<float, 16, kOneState>(p, stream);
+    return all ? launch_n<bf16_t, 16, kAllStates, 2>(p, stream) : launch_n<bf16_t, 16, kOneState, 2>(p, stream);
+  return all ? launch_n<float, 16, kAllStates, 2>(p, stream) : launch_n<float, 16, kOneState, 2>(p, stream);
 }
 
 }  // namespace ss

@@ -114,12 +114,16 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // delta = u - (w - 1) (exact by Sterbenz), since log(1 + u) = log(w) +
 // log(1 + delta / w) and |delta| <= 2^-24 makes the second term delta to
 // within 2^-24 relative (the compensated log1p of Goldberg, 1991).
+//
+// max(v, 0) + l is formed as 0.5 (v + |v|) + l: v + |v| is exactly 2 max(v, 0),
+// so the result is the same number, in one add and one FMA (fmaxf would cost
+// an extra canonicalising max on its input).
 __device__ __forceinline__ float softplus_f32(float v) {
   const float u = fast_exp2(-__builtin_fabsf(v) * kLog2e);
   const float w = 1.0f + u;
   const float delta = u - (w - 1.0f);
   const float l = __builtin_fmaf(fast_log2(w), kLn2, delta);
-  return __builtin_fmaxf(v, 0.0f) + l;
+  return __builtin_fmaf(0.5f, v + __builtin_fabsf(v), l);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}); e^{-z} = inf gives -0.
@@ -151,10 +155,17 @@ __device__ __forceinline__ float dpp_or(float old, float v) {
 // Boundary Resetting, binop). Hillis-Steele steps of 1, 2, 4, 8 lanes; a lane
 // whose partner falls outside the row has its DPP write disabled and keeps its
 // value, which is combining with the identity (1, 0). In each step the B
-// update reads the lane's A before the A update overwrites it. The leading
-// s_nop covers the VALU-write -> DPP-read wait states (2 on gfx9); inside
-// the block each DPP read is at least 3 instructions after the write.
-__device__ __forceinline__ void row16_inclusive_scan(float& A, float& B) {
+// update reads the lane's A before the A update overwrites it; the last step
+// needs no A update, so A is left holding the products over 8-lane windows.
+//
+// Then the entry into the lane's own tokens: lanes 1..15 take the state that
+// lane l-1 ends with, h <- a0 * B[l-1] + h (h holds the first token's b0 on
+// entry), in one DPP FMA; lane 0's DPP write is disabled, so it keeps h
+// (which must already hold its first token's state, from the carry).
+//
+// The leading s_nops cover the VALU-write -> DPP-read wait states (2 on gfx9);
+// inside the block each DPP read is at least 3 instructions after the write.
+__device__ __forceinline__ void row16_scan_and_enter(float A, float& B, float& h, float a0) {
   asm volatile(
       "s_nop 1\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
@@ -167,8 +178,10 @@ __device__ __forceinline__ void row16_inclusive_scan(float& A, float& B) {
       "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-      : "+v"(A), "+v"(B));
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %2, %1, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B), "+v"(h)
+      : "v"(a0));
 }
 
 }  // namespace ss

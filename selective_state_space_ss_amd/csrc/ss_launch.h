@@ -65,6 +65,9 @@ struct GatedParams {
 // launch_scan_fwd picks between the chunked scan (scan_fwd.hip) and the
 // row-parallel walk (scan_rows.hip, launch_scan_rows) by shape.
 hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream);
+// The chunked scan's instances with a reset mask (scan_fwd_reset.hip), at K
+// tokens per lane (16 or 32).
+hipError_t launch_scan_fwd_reset(const ScanParams& p, bool io_bf16, int K, hipStream_t stream);
 hipError_t launch_scan_rows(const ScanParams& p, bool io_bf16, hipStream_t stream);
 // The scan that also writes per-token states (scan_states.hip): p.states
 // receives [batch, channels, N, L] (p.time_step < 0) or the state after token
