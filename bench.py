@@ -424,6 +424,42 @@ def measure_attention(ss, stream, reps: int = 20):
 PRODUCER_SHAPE = (8, 5120, 2048, 4, 160)   # batch, channels, seq, conv width, dt rank
 
 
+def measure_fused_conv(ss, P, w, stream, rates, reps: int = 20):
+    """ss_scan_fwd_conv (the conv1d + SiLU of width 4 fused into the scan, x
+    never written) at the Mamba-2.8B prompt shape, next to the two-kernel
+    chain it replaces: ss_conv1d_silu, then ss_scan_fwd on the written x.
+    Algorithmic bytes of the fused call: the scan's with x_pre in place of x,
+    plus the conv weights; of the chain: the conv's (read x_pre, write x) plus
+    the scan's."""
+    import torch
+    from selective_state_space_ss_amd.workloads import algorithmic_bytes, make_producer_case
+    width = 4
+    c = make_producer_case(1030, w.batch, w.channels, w.seqlen, width, 1, "bf16", device="cuda")
+    y = torch.empty_like(P["x"])
+    h = torch.empty(w.batch, w.channels, w.state_dim, dtype=torch.float32, device="cuda")
+    x = torch.empty_like(P["x"])
+    fused = lambda: ss.ss_scan_fwd_conv(c["x_pre"], P["dt"], P["A"], P["B"], P["C"], c["conv_w"], c["conv_b"],
+                                        D=P["D"], z=P["z"], dt_bias=P["dt_bias"], h0=P["h0"], y=y, h_last=h)
+
+    def chain():
+        ss.ss_conv1d_silu(c["x_pre"], c["conv_w"], c["conv_b"], out=x)
+        ss.ss_scan_fwd(x, P["dt"], P["A"], P["B"], P["C"], D=P["D"], z=P["z"], dt_bias=P["dt_bias"], h0=P["h0"],
+                       y=y, h_last=h)
+    us_f = time_launches(fused, stream, reps)
+    us_c = time_launches(chain, stream, reps)
+    scan_bytes = algorithmic_bytes(w)
+    conv_extra = w.channels * (width + 1) * 4
+    r = scan_roofline(w, us_f, rates)
+    r["algorithmic_bytes"] = scan_bytes + conv_extra
+    r["GB_s"] = round((scan_bytes + conv_extra) / (us_f * 1e-6) / 1e9, 1)
+    return {"shape": {"batch": w.batch, "channels": w.channels, "state_dim": w.state_dim, "seq": w.seqlen,
+                      "width": width, "io": "bf16"},
+            "fused": r,
+            "conv1d_silu_then_scan_us": round(us_c, 2),
+            "chain_algorithmic_bytes": scan_bytes + conv_extra + 2 * w.batch * w.channels * w.seqlen * 2,
+            "speedup": round(us_c / us_f, 3)}
+
+
 def measure_producers(ss, stream, reps: int = 20):
     """The scan's input side at the Mamba-2.8B layer shape (batch 8, channels
     5120, seq 2048, bf16): ss_conv1d_silu (width 4; bytes: read x_pre, write
@@ -732,6 +768,7 @@ def main():
                          "ss_gated_scan": measure_gated(ss, stream),
                          "ss_effective_attention": measure_attention(ss, stream),
                          "producers": measure_producers(ss, stream),
+                         "ss_scan_fwd_conv": measure_fused_conv(ss, P, wp, stream, rates),
                          "stream_copy_1GiB": measure_copy(stream)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 7
+#define SS_ABI_VERSION 8
 #define SS_MAX_STATE_DIM 64
 #define SS_MAX_GATED_DK 256
 #define SS_MAX_CONV_WIDTH 8
@@ -158,6 +158,30 @@ ss_status ss_scan_fwd(const ss_scan_args* args, void* stream);
  * by HBM bandwidth; the single-step form costs about what ss_scan_fwd does.
  */
 ss_status ss_scan_fwd_states(const ss_scan_args* args, float* states, int64_t time_step, void* stream);
+
+/*
+ * The prompt scan with its input-side producer fused in (nnterp
+ * "selective_scan" page, class docstring: the scan's x is the causal conv1d
+ * output after SiLU; TransformerLens "ssm_mixer" page: x is the post-conv
+ * SiLU input). Here args->x holds x_pre, the conv input, [batch, channels,
+ * seqlen] in io_dtype; the kernel forms
+ *
+ *   x[b, c, t] = silu(conv_b[c] + sum_{k<width} conv_w[c, k] * x_pre[b, c, t - (width-1) + k])
+ *
+ * in fp32 (not rounded to io_dtype, never written to memory) and scans it,
+ * as ss_conv1d_silu followed by ss_scan_fwd would, except that x keeps fp32
+ * precision. A tap before position 0 reads 0, and with args->reset so does a
+ * tap before the first token of the current document (as ss_conv1d_silu).
+ *
+ *   conv_w      : [channels, width] float32; width in [1, SS_MAX_CONV_WIDTH]
+ *                 (else SS_ERR_UNSUPPORTED)
+ *   conv_b      : [channels] float32, or NULL (= 0)
+ *
+ * Everything else is ss_scan_fwd's: arguments, outputs (conv_w and conv_b
+ * must not overlap y or h_last), conventions and errors.
+ */
+ss_status ss_scan_fwd_conv(const ss_scan_args* args, const float* conv_w, const float* conv_b, int64_t width,
+                           void* stream);
 
 /*
  * Single-token decode update of a cached state, in place (nnterp

@@ -25,6 +25,11 @@ and the dt_proj projection that makes dt):
     ss_conv1d_silu(x_pre, conv_w, conv_b=None, reset=None) -> x
     ss_dt_proj(w_dt, delta, dt_bias=None, apply_softplus=False) -> dt
 
+and the scan with the conv1d + SiLU fused in (x made in registers from
+x_pre, never written to memory):
+
+    ss_scan_fwd_conv(x_pre, dt, A, B, C, conv_w, conv_b=None, D=None, ...) -> (y, h_last)
+
 and the scan's effective attention of the TransformerLens "ssm_mixer" page:
 
     ss_effective_attention(dt, A, B, C, dt_bias=None, include_dt_scaling=False,
@@ -47,6 +52,7 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     ss_scan_fwd,
+    ss_scan_fwd_conv,
     ss_scan_fwd_states,
     ss_state_update,
     status_str,

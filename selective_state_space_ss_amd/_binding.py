@@ -61,6 +61,8 @@ def load_library() -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.ss_scan_fwd.restype = i32
     lib.ss_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), vp]
+    lib.ss_scan_fwd_conv.restype = i32
+    lib.ss_scan_fwd_conv.argtypes = [ctypes.POINTER(ScanArgs), vp, vp, i64, vp]
     lib.ss_scan_fwd_states.restype = i32
     lib.ss_scan_fwd_states.argtypes = [ctypes.POINTER(ScanArgs), vp, i64, vp]
     lib.ss_gated_scan.restype = i32
@@ -136,6 +138,29 @@ def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=Non
     rc = load_library().ss_scan_fwd(ctypes.byref(args), _stream_handle(dev, stream))
     if rc != SS_OK:
         raise SSError(rc, "ss_scan_fwd")
+    return y, h_last
+
+
+def ss_scan_fwd_conv(x_pre, dt, A, B, C, conv_w, conv_b=None, D=None, z=None, dt_bias=None, h0=None, reset=None,
+                     dt_softplus: bool = True, *, y=None, h_last=None, return_last_state: bool = True,
+                     stream=None) -> Tuple:
+    """The prompt scan with its x made in the same kernel from x_pre by the
+    causal conv1d + SiLU (x never written to memory): conv_w [channels,
+    width] and conv_b [channels] float32, width <= 8; x_pre in place of x,
+    every other argument as ss_scan_fwd. Returns (y, h_last)."""
+    import torch
+    y, h_last, args, dev = _scan_args(x_pre, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
+                                      return_last_state)
+    channels = x_pre.shape[1]
+    if conv_w.dim() != 2 or conv_w.shape[0] != channels:
+        raise ValueError("conv_w must be [channels, width]")
+    _check(conv_w, "conv_w", (channels, conv_w.shape[1]), torch.float32, dev)
+    if conv_b is not None:
+        _check(conv_b, "conv_b", (channels,), torch.float32, dev)
+    rc = load_library().ss_scan_fwd_conv(ctypes.byref(args), _ptr(conv_w), _ptr(conv_b), conv_w.shape[1],
+                                         _stream_handle(dev, stream))
+    if rc != SS_OK:
+        raise SSError(rc, "ss_scan_fwd_conv")
     return y, h_last
 
 

@@ -24,7 +24,7 @@ PROBE_LIB = os.path.join(PKG, "libssprobe.so")
 PROBE_SOURCES = ["probe_issue.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_fwd_reset.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
+SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_fwd_reset.hip", "scan_fwd_conv.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -69,9 +69,84 @@ constexpr int min_waves_per_simd() {
   return K == 32 ? 2 : ((RESET || sizeof(IoT) == 4) ? 3 : 4);
 }
 
-template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES>
+// The fused producer of x (nnterp "selective_scan" page, class docstring; the
+// ssm_mixer page's x is the post-conv SiLU input): for this lane's K tokens,
+//   x_t = silu(conv_b + sum_{k<W} conv_w[k] * x_pre[t - (W-1) + k]),
+// a depthwise causal convolution, in fp32 and never rounded or stored. A tap
+// before position 0, or before the current document's first token (a reset
+// mask; bit 8 + j of `starts` marks token tb + j, bits 0..7 the 8 tokens
+// before the lane), reads 0. The taps are taken through a window of the CW - 1
+// previous x_pre values, which a document start clears, so each token costs
+// CW FMAs (weights past W are 0) plus, with resets, CW - 1 selects.
+template <typename IoT, int K, int CW, bool RESET>
+__device__ __forceinline__ void conv_silu_lane(const IoT* __restrict__ xpg, int64_t tb, int64_t L, bool full,
+                                               const float* __restrict__ wrow, int Wd, float cb, uint32_t starts,
+                                               float* xv) {
+  constexpr int VEC = Io<IoT>::kVec;
+  float xp[K], hp[8];  // this lane's x_pre, and the 8 tokens before it
+  if (full) {
+#pragma unroll
+    for (int v = 0; v < K / VEC; ++v) load_vec16(xpg + tb + v * VEC, xp + v * VEC);
+    if (tb >= 8) {
+#pragma unroll
+      for (int v = 0; v < 8 / VEC; ++v) load_vec16(xpg + tb - 8 + v * VEC, hp + v * VEC);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hp[u] = tb - 8 + u >= 0 ? Io<IoT>::to_f32(xpg[tb - 8 + u]) : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) xp[j] = tb + j < L ? Io<IoT>::to_f32(xpg[tb + j]) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = tb - 8 + u;
+      hp[u] = (s >= 0 && s < L) ? Io<IoT>::to_f32(xpg[s]) : 0.0f;
+    }
+  }
+  // wp[i]: the weight of the tap at t - (CW - 1) + i (conv_w[W - CW + i]), 0 for i < CW - W
+  float wp[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) wp[i] = i >= CW - Wd ? wrow[Wd - CW + i] : 0.0f;
+  // the window before token 0: positions -(CW - 1) .. -1, cleared at document starts
+  float win[CW > 1 ? CW - 1 : 1];
+#pragma unroll
+  for (int i = 0; i < CW - 1; ++i) win[i] = 0.0f;
+#pragma unroll
+  for (int q = -(CW - 1); q < 0; ++q) {
+    if constexpr (RESET) {
+      if ((starts >> (8 + q)) & 1u) {
+#pragma unroll
+        for (int i = 0; i < CW - 1; ++i) win[i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i + 1 < CW - 1; ++i) win[i] = win[i + 1];
+    if constexpr (CW > 1) win[CW - 2] = hp[8 + q];
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if constexpr (RESET) {
+      if ((starts >> (8 + j)) & 1u) {
+#pragma unroll
+        for (int i = 0; i < CW - 1; ++i) win[i] = 0.0f;
+      }
+    }
+    float acc = __builtin_fmaf(wp[CW - 1], xp[j], cb);
+#pragma unroll
+    for (int i = 0; i < CW - 1; ++i) acc = __builtin_fmaf(wp[i], win[i], acc);
+    xv[j] = silu_f32(acc);
+#pragma unroll
+    for (int i = 0; i + 1 < CW - 1; ++i) win[i] = win[i + 1];
+    if constexpr (CW > 1) win[CW - 2] = xp[j];
+  }
+}
+
+// CW: 0, or the tap bound (4 or 8) of the fused causal conv1d + SiLU that
+// makes x from x_pre (p.x is then x_pre; see conv_silu_lane).
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0>
 __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void scan_fwd_kernel(
     const ScanParams p) {
+  static_assert(CW == 0 || (K == 16 && STATES == kNoStates), "the fused conv runs at 16 tokens per lane");
   using S = Shape<K, W>;
   constexpr int T = S::kT;
   constexpr int KP = K + 4;  // LDS stride of one lane's K values (spreads the banks)
@@ -147,18 +222,19 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     if (full) {
 #pragma unroll
       for (int v = 0; v < K / VEC; ++v) {
-        load_vec16(xg + tb + v * VEC, xv + v * VEC);
+        if constexpr (CW == 0) load_vec16(xg + tb + v * VEC, xv + v * VEC);
         load_vec16(dg + tb + v * VEC, dv + v * VEC);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const bool in = tb + j < L;
-        xv[j] = in ? Io<IoT>::to_f32(xg[tb + j]) : 0.0f;
+        if constexpr (CW == 0) xv[j] = in ? Io<IoT>::to_f32(xg[tb + j]) : 0.0f;
         dv[j] = in ? Io<IoT>::to_f32(dg[tb + j]) : 0.0f;
       }
     }
     uint32_t rbits = 0;  // bit j: token tb + j starts a document
+    uint32_t hbits = 0;  // (fused conv) bit u: token tb - 8 + u starts a document
     if constexpr (RESET) {
       if (full && p.reset_vec) {
 #pragma unroll
@@ -169,12 +245,29 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
           for (int i = 0; i < 16; ++i)
             rbits |= (((ws[i >> 2] >> (8 * (i & 3))) & 0xffu) ? 1u : 0u) << (16 * v + i);
         }
+        if constexpr (CW > 0) {
+          if (tb >= 8) {
+            const uint2 w = *reinterpret_cast<const uint2*>(rg + tb - 8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hbits |= ((((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xffu) ? 1u : 0u) << i;
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < K; ++j)
           if (tb + j < L && rg[tb + j]) rbits |= 1u << j;
+        if constexpr (CW > 0) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int64_t s = tb - 8 + u;
+            if (s >= 0 && s < L && rg[s]) hbits |= 1u << u;
+          }
+        }
       }
     }
+    if constexpr (CW > 0)
+      conv_silu_lane<IoT, K, CW, RESET>(xg, tb, L, full, p.conv_w + c * p.conv_width, p.conv_width,
+                                        p.conv_b ? p.conv_b[c] : 0.0f, hbits | (rbits << 8), xv);
 
     // 2. stage this chunk's B and C (fp32) of a group of coordinates for the
     // whole block, between two barriers (the first: the previous readers are
@@ -370,14 +463,14 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET>())) void
     for (int n = tl; n < N; n += kRowLanes) p.h_last[(b * p.channels + c) * N + n] = sCarry[slot + n];
 }
 
-template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES>
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0>
 hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
   ScanParams p = p0;
   p.chan_blocks = (p.channels + Shape<K, W>::kChan - 1) / Shape<K, W>::kChan;
   const int64_t blocks = p.batch * p.chan_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES, CW>),
                          dim3((unsigned)blocks), dim3(Shape<K, W>::kThreads), args, 0, stream);
 }
 
@@ -390,7 +483,7 @@ hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
 // mask, 1 = with one, 2 = both (picked at run time). The plain scan keeps the
 // two sets in separate files, each built with the machine scheduler that
 // measured faster for it.
-template <typename IoT, int K, int NMAX, int STATES, int RESETS>
+template <typename IoT, int K, int NMAX, int STATES, int RESETS, int CW = 0>
 hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   const bool gate = p.z != nullptr, reset = p.reset != nullptr;
   // 8-wave blocks when 4 waves fit per SIMD (two blocks per CU), else 4-wave
@@ -401,13 +494,13 @@ hipError_t launch_flags(const ScanParams& p, hipStream_t stream) {
   constexpr int WR = 4;
   if constexpr (RESETS != 0) {
     if (reset || RESETS == 1) {
-      if (gate) return launch_t<IoT, K, WR, NMAX, true, true, STATES>(p, stream);
-      return launch_t<IoT, K, WR, NMAX, false, true, STATES>(p, stream);
+      if (gate) return launch_t<IoT, K, WR, NMAX, true, true, STATES, CW>(p, stream);
+      return launch_t<IoT, K, WR, NMAX, false, true, STATES, CW>(p, stream);
     }
   }
   if constexpr (RESETS != 1) {
-    if (gate) return launch_t<IoT, K, W, NMAX, true, false, STATES>(p, stream);
-    return launch_t<IoT, K, W, NMAX, false, false, STATES>(p, stream);
+    if (gate) return launch_t<IoT, K, W, NMAX, true, false, STATES, CW>(p, stream);
+    return launch_t<IoT, K, W, NMAX, false, false, STATES, CW>(p, stream);
   }
   return hipErrorInvalidValue;
 }

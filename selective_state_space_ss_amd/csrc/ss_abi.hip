@@ -9,9 +9,15 @@ namespace {
 
 bool vec16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The shared body of ss_scan_fwd and ss_scan_fwd_states (states == nullptr:
-// the plain scan).
-int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, void* stream) {
+struct ConvArgs {
+  const float* w;
+  const float* b;
+  int64_t width;
+};
+
+// The shared body of ss_scan_fwd, ss_scan_fwd_states (states != nullptr) and
+// ss_scan_fwd_conv (conv != nullptr).
+int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, const ConvArgs* conv, void* stream) {
   const int64_t batch = a.batch, channels = a.channels, state_dim = a.state_dim, seqlen = a.seqlen;
   const int io_dtype = a.io_dtype;
   const void *x = a.x, *dt = a.dt, *z = a.z, *B = a.B, *C = a.C;
@@ -20,6 +26,7 @@ int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, void* st
   bool noop = false;
   ss_status st = ss::validate_scan(a, &noop);
   if (st == SS_OK && states) st = ss::validate_scan_states(a, states, time_step);
+  if (st == SS_OK && !noop && conv) st = ss::validate_scan_conv(a, conv->w, conv->b, conv->width);
   if (st != SS_OK || noop) return st;
   if (seqlen == 0 && a.h_last == nullptr) return SS_OK;
   if (ss::scan_fwd_blocks(batch, channels) > 0x7fffffff) return SS_ERR_SHAPE;
@@ -49,8 +56,15 @@ int scan_entry(const ss::ScanArgs& a, float* states, int64_t time_step, void* st
   p.states = states;
   p.time_step = time_step;
   p.states_vec = (seqlen % 4 == 0) && vec16(states);
-  const hipError_t e = states ? ss::launch_scan_states(p, bf16, static_cast<hipStream_t>(stream))
-                              : ss::launch_scan_fwd(p, bf16, static_cast<hipStream_t>(stream));
+  if (conv) {
+    p.conv_w = conv->w;
+    p.conv_b = conv->b;
+    p.conv_width = (int)conv->width;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = states ? ss::launch_scan_states(p, bf16, s)
+                       : conv ? ss::launch_scan_fwd_conv(p, bf16, s)
+                              : ss::launch_scan_fwd(p, bf16, s);
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
@@ -60,12 +74,19 @@ extern "C" {
 
 ss_status ss_scan_fwd(const ss_scan_args* args, void* stream) {
   if (!args) return SS_ERR_NULL;
-  return static_cast<ss_status>(scan_entry(*args, nullptr, -1, stream));
+  return static_cast<ss_status>(scan_entry(*args, nullptr, -1, nullptr, stream));
 }
 
 ss_status ss_scan_fwd_states(const ss_scan_args* args, float* states, int64_t time_step, void* stream) {
   if (!args || !states) return SS_ERR_NULL;
-  return static_cast<ss_status>(scan_entry(*args, states, time_step, stream));
+  return static_cast<ss_status>(scan_entry(*args, states, time_step, nullptr, stream));
+}
+
+ss_status ss_scan_fwd_conv(const ss_scan_args* args, const float* conv_w, const float* conv_b, int64_t width,
+                           void* stream) {
+  if (!args) return SS_ERR_NULL;
+  const ConvArgs conv{conv_w, conv_b, width};
+  return static_cast<ss_status>(scan_entry(*args, nullptr, -1, &conv, stream));
 }
 
 ss_status ss_state_update(const ss_update_args* args, void* stream) {
@@ -200,7 +221,9 @@ const char* ss_status_str(int status) {
     case SS_ERR_NULL: return "SS_ERR_NULL: a required pointer is NULL";
     case SS_ERR_SHAPE: return "SS_ERR_SHAPE: a size is negative or too large";
     case SS_ERR_DTYPE: return "SS_ERR_DTYPE: io_dtype is not SS_F32 or SS_BF16";
-    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED: state_dim outside [1, 64] (gated scan: dk outside [1, 256] or dv < 1)";
+    case SS_ERR_UNSUPPORTED:
+      return "SS_ERR_UNSUPPORTED: state_dim outside [1, 64] (gated scan: dk outside [1, 256] or dv < 1; conv width "
+             "outside [1, 8]; dt_proj rank < 1)";
     case SS_ERR_ALIAS: return "SS_ERR_ALIAS: an output overlaps an input";
     case SS_ERR_HIP: return "SS_ERR_HIP: the HIP runtime failed to launch the kernel";
     case SS_ERR_ALIGN: return "SS_ERR_ALIGN: a pointer is not aligned to its element size";

@@ -29,6 +29,10 @@ struct ScanParams {
   float* states;      // per-token states (launch_scan_states only)
   int64_t time_step;  // < 0: every token's state; else the state after this token
   int states_vec;     // states 16-byte aligned and L a multiple of 4
+  // fused conv1d + SiLU (launch_scan_fwd_conv only): x is then x_pre
+  const float* conv_w;  // [channels, conv_width]
+  const float* conv_b;  // [channels] or nullptr
+  int conv_width;
 };
 
 struct UpdateParams {
@@ -65,6 +69,10 @@ struct GatedParams {
 // launch_scan_fwd picks between the chunked scan (scan_fwd.hip) and the
 // row-parallel walk (scan_rows.hip, launch_scan_rows) by shape.
 hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream);
+// The prompt scan with its x made in the kernel from x_pre (p.x) by the
+// causal conv1d + SiLU (scan_fwd_conv.hip): 16 tokens per lane, N <= 16 or
+// <= 64 instances, conv width <= 8.
+hipError_t launch_scan_fwd_conv(const ScanParams& p, bool io_bf16, hipStream_t stream);
 // The chunked scan's instances with a reset mask (scan_fwd_reset.hip), at K
 // tokens per lane (16 or 32).
 hipError_t launch_scan_fwd_reset(const ScanParams& p, bool io_bf16, int K, hipStream_t stream);

@@ -100,6 +100,24 @@ inline ss_status validate_scan_states(const ScanArgs& a, const float* states, in
   return SS_OK;
 }
 
+// The fused conv's extra arguments of ss_scan_fwd_conv (after validate_scan
+// has accepted the scan's): the width, the weights, and no overlap of the
+// weights with the outputs.
+inline ss_status validate_scan_conv(const ScanArgs& a, const float* conv_w, const float* conv_b, int64_t width) {
+  if (width < 1 || width > SS_MAX_CONV_WIDTH) return SS_ERR_UNSUPPORTED;
+  if (!conv_w) return SS_ERR_NULL;
+  if (!aligned(conv_w, 4) || (conv_b && !aligned(conv_b, 4))) return SS_ERR_ALIGN;
+  const int64_t es = a.io_dtype == SS_BF16 ? 2 : 4;
+  int64_t rows, tok, tok_bytes, st, st_bytes, wn, w_bytes, b_bytes;
+  if (!mul_ok(a.batch, a.channels, &rows) || !mul_ok(rows, a.seqlen, &tok) || !mul_ok(tok, es, &tok_bytes) ||
+      !mul_ok(rows, a.state_dim, &st) || !mul_ok(st, 4, &st_bytes) || !mul_ok(a.channels, width, &wn) ||
+      !mul_ok(wn, 4, &w_bytes) || !mul_ok(a.channels, 4, &b_bytes))
+    return SS_ERR_SHAPE;
+  const Span w(conv_w, w_bytes), cb(conv_b, b_bytes), y(a.y, a.seqlen > 0 ? tok_bytes : 0), hl(a.h_last, st_bytes);
+  if (w.overlaps(y) || w.overlaps(hl) || cb.overlaps(y) || cb.overlaps(hl)) return SS_ERR_ALIAS;
+  return SS_OK;
+}
+
 // Inputs of the scalar-gated state scan, in ABI order; see ss_gated_scan.
 struct GatedArgs {
   int64_t batch, seqlen, dk, dv;

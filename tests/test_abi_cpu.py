@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["ss_abi_version", "ss_conv1d_silu", "ss_dt_proj", "ss_effective_attention",
-                                    "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_states", "ss_state_update",
-                                    "ss_status_str"]
+                                    "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_conv", "ss_scan_fwd_states",
+                                    "ss_state_update", "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 7
+    assert ss.abi_version() == 8
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -71,6 +71,24 @@ def upd_call(lib, batch=2, channels=8, N=16, io=1, state=1 * MB, x=2 * MB, dt=3 
     a = UpdateArgs(batch=batch, channels=channels, state_dim=N, io_dtype=io, state=state, x=x, dt=dt, z=z, B=B, C=C,
                    A=A, D=D, dt_bias=bias, dt_softplus=1, y=y)
     return lib.ss_state_update(ctypes.byref(a), None)
+
+
+def conv_scan_call(lib, w=9 * MB, b=None, width=4, **kw):
+    return lib.ss_scan_fwd_conv(ctypes.byref(scan_args(**kw)), w, b, width, None)
+
+
+def test_scan_conv_validation(lib):
+    assert conv_scan_call(lib, width=0) == UNSUP
+    assert conv_scan_call(lib, width=9) == UNSUP
+    assert conv_scan_call(lib, w=None) == NULL
+    assert conv_scan_call(lib, w=9 * MB + 2) == ALIGN
+    assert conv_scan_call(lib, b=10 * MB + 1) == ALIGN
+    assert conv_scan_call(lib, w=6 * MB) == ALIAS                      # weights over y
+    assert conv_scan_call(lib, b=7 * MB, h_last=7 * MB) == ALIAS        # bias over h_last
+    assert conv_scan_call(lib, x=None) == NULL                          # x_pre is the scan's x
+    assert conv_scan_call(lib, io=4) == DTYPE
+    assert conv_scan_call(lib, batch=0, w=None) == OK                   # an empty problem is a no-op
+    assert lib.ss_scan_fwd_conv(None, 9 * MB, None, 4, None) == NULL
 
 
 def test_null_argument_structs(lib):
@@ -266,6 +284,8 @@ def test_launch_without_a_device_returns_hip_error(lib):
     assert scan_call(lib, io=0, z=7 * MB, h0=8 * MB, h_last=9 * MB, reset=10 * MB) == HIP
     assert states_call(lib) == HIP
     assert states_call(lib, time_step=3) == HIP
+    assert conv_scan_call(lib) == HIP
+    assert conv_scan_call(lib, reset=10 * MB, width=7) == HIP
     assert upd_call(lib) == HIP
     assert gated_call(lib) == HIP
     assert attn_call(lib) == HIP
