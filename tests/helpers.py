@@ -79,3 +79,20 @@ def check_close(gpu, ref, rtol, atol, what):
 
 def to_dev(inp, device="cuda"):
     return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
+
+
+# The prompt-scan kernel variants the GPU tests run: the chunked scan at 16
+# and at 32 tokens per lane, its split form (two waves per group of rows,
+# each on half of the state coordinates) in 4- and 8-wave blocks, and the
+# row-parallel walk. The library picks one by shape; SS_SCAN_KERNEL,
+# SS_SCAN_TOKENS_PER_LANE and SS_SCAN_SPLIT, read at every call, force one.
+# (The split form takes no reset mask: with one, the split variants run the
+# plain chunked scan.)
+SCAN_KERNELS = ["chunked", "chunked32", "split4", "split8", "rows"]
+RESET_SCAN_KERNELS = ["chunked", "chunked32", "rows"]
+
+
+def force_scan_kernel(monkeypatch, kind):
+    monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if kind == "rows" else "chunked")
+    monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if kind == "chunked32" else "16")
+    monkeypatch.setenv("SS_SCAN_SPLIT", kind[len("split"):] if kind.startswith("split") else "off")

@@ -7,17 +7,15 @@ import torch
 
 import selective_state_space_ss_amd as ss
 from selective_state_space_ss_amd.workloads import make_case
-from tests.helpers import TOL, TOL_STATE, check_close, np64, to_dev
+from tests.helpers import SCAN_KERNELS, TOL, TOL_STATE, check_close, force_scan_kernel, np64, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["chunked", "chunked32", "rows"])
+@pytest.fixture(params=SCAN_KERNELS)
 def scan_kernel(request, monkeypatch):
-    """Both prompt-scan kernels, the chunked one at 16 and at 32 tokens per
-    lane (SS_SCAN_KERNEL and SS_SCAN_TOKENS_PER_LANE force one)."""
-    monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if request.param == "rows" else "chunked")
-    monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if request.param == "chunked32" else "16")
+    """Every prompt-scan kernel variant (tests/helpers.py, SCAN_KERNELS)."""
+    force_scan_kernel(monkeypatch, request.param)
     return request.param
 
 

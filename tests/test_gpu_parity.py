@@ -11,20 +11,24 @@ import torch
 import oracle
 import selective_state_space_ss_amd as ss
 from selective_state_space_ss_amd.workloads import WORKLOADS, make_case, make_decode_case, make_inputs
-from tests.helpers import (TOL, TOL_STATE, check_close, io_name, np64, oracle_scan_full, oracle_scan_rows,
-                           sample_rows, to_dev)
+from tests.helpers import (RESET_SCAN_KERNELS, SCAN_KERNELS, TOL, TOL_STATE, check_close, force_scan_kernel,
+                           io_name, np64, oracle_scan_full, oracle_scan_rows, sample_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["chunked", "chunked32", "rows"])
+@pytest.fixture(params=SCAN_KERNELS)
 def scan_kernel(request, monkeypatch):
-    """Both prompt-scan kernels, the chunked one at 16 and at 32 tokens per
-    lane (the library picks by shape; the SS_SCAN_KERNEL and
-    SS_SCAN_TOKENS_PER_LANE overrides, read at every call, force one)."""
-    monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if request.param == "rows" else "chunked")
-    monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if request.param == "chunked32" else "16")
+    """Every prompt-scan kernel variant (tests/helpers.py, SCAN_KERNELS)."""
+    force_scan_kernel(monkeypatch, request.param)
+    return request.param
+
+
+@pytest.fixture(params=RESET_SCAN_KERNELS)
+def reset_scan_kernel(request, monkeypatch):
+    """The variants that take a reset mask."""
+    force_scan_kernel(monkeypatch, request.param)
     return request.param
 
 
@@ -83,8 +87,8 @@ def test_packed_reset_default_kernel_choice(monkeypatch):
     """The library's own choice of tokens per lane (no override): with a reset
     mask and a long sequence on few channels it takes 32 tokens per lane;
     every element against the oracle."""
-    monkeypatch.delenv("SS_SCAN_TOKENS_PER_LANE", raising=False)
-    monkeypatch.delenv("SS_SCAN_KERNEL", raising=False)
+    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_SPLIT"):
+        monkeypatch.delenv(k, raising=False)
     print("default kernel choice: bf16 1 x 64 x 16 x 8192 with resets", flush=True)
     inp = make_case(905, 1, 64, 16, 8192, "bf16", gate=True, h0=True, reset_mean_doc=512)
     compare_full(inp, what="default choice 1x64x8192")
@@ -131,12 +135,12 @@ EDGE_KINDS = ["every_token", "lane16", "chunk256", "lane32", "chunk512", "stradd
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("kind", EDGE_KINDS)
-def test_reset_edges(kind, io, scan_kernel):
+def test_reset_edges(kind, io, reset_scan_kernel):
     """Resets placed on every token, on lane and chunk boundaries, in adjacent
     pairs straddling them, and with an initial state ("s6_reset" post,
     Enforced Boundary Resetting: the state is zeroed before a document's
     first token; a reset at t = 0 discards h0)."""
-    print(f"reset edges {kind} io={io} kernel={scan_kernel}", flush=True)
+    print(f"reset edges {kind} io={io} kernel={reset_scan_kernel}", flush=True)
     L = 1100
     inp = make_case(920 + EDGE_KINDS.index(kind), 2, 19, 16, L, io, gate=True, h0=True)
     inp["reset"] = _edge_mask(kind, 2, L)
@@ -303,3 +307,18 @@ def test_decode_shapes(io, N, gate):
                                  dt_bias=np64(inp["dt_bias"]))
     check_close(np64(y), yr, *TOL[io], "decode y")
     check_close(np64(state), sr, *TOL_STATE, "decode state")
+
+
+@pytest.mark.parametrize("split", ["4", "8"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 9, 12, 16, 17])
+def test_split_form_state_dims(N, io, split, monkeypatch):
+    """The split form (each of two waves on half of a row group's state
+    coordinates, y summed through LDS) at every instantiated state width, a
+    ragged channel count (21: partial 8- and 16-row blocks) and a ragged tail
+    over several chunks; N = 17 is past the split form's range and takes the
+    plain scan."""
+    force_scan_kernel(monkeypatch, "split" + split)
+    print(f"split form {split} waves io={io} N={N}", flush=True)
+    inp = make_case(330 + N, 2, 21, N, 777, io, gate=N % 2 == 0, h0=N % 3 != 0)
+    compare_full(inp, what=f"split{split} {io} N={N}")
