@@ -4,9 +4,10 @@
 //
 // Work decomposition. A channel row (b, c) is owned by one 16-lane DPP row of
 // a wavefront: a wave holds 4 channels of one batch row, a block of W waves
-// 4W channels of that batch row. The sequence is walked in chunks of 16*K
-// tokens; inside a chunk lane l of a row owns the K consecutive tokens
-// [l*K, (l+1)*K). Per chunk:
+// 4W channels of that batch row. (Launches with few rows give a row 32 or 64
+// lanes instead: 2 or 1 channels per wave; RL below.) The sequence is walked
+// in chunks of 16*K tokens; inside a chunk lane l of a row owns the K
+// consecutive tokens [l*K, (l+1)*K). Per chunk:
 //   1. each lane loads its K tokens of x and dt, coalesced along seq;
 //   2. the block stages the chunk's B and C (shared by all its channels:
 //      one group, nnterp "selective_scan" page) into LDS as fp32;
@@ -54,23 +55,26 @@ enum StatesOut { kNoStates = 0, kAllStates = 1, kOneState = 2 };
 constexpr int kRowLanes = 16;
 constexpr int kRowsPerWave = 4;
 
-// SPLIT = 2: two waves share each group of 4 rows, each taking half of the
-// state coordinates (the split form below), so a block of W waves holds 2 W
-// rows instead of 4 W.
-template <int K, int W, int SPLIT = 1>
+// Launch forms for few rows (launch_flags).
+enum Form { kPlain = 0, kRows32w4 = 1, kRows32w8 = 2, kRows64w4 = 3 };
+
+// RL: lanes per row (16, 32 or 64): a wave holds 64 / RL rows, and a chunk
+// is RL K tokens.
+template <int K, int W, int RL = kRowLanes>
 struct Shape {
   static constexpr int kThreads = 64 * W;
-  static constexpr int kChan = kRowsPerWave * W / SPLIT;  // channels per block
-  static constexpr int kT = kRowLanes * K;                // tokens per chunk
+  static constexpr int kRows = 64 / RL;    // rows per wave
+  static constexpr int kChan = kRows * W;  // channels per block
+  static constexpr int kT = RL * K;        // tokens per chunk
 };
 
 // Waves per SIMD the register budget is set for (launch bound). K = 16 with
 // bf16 I/O and no reset mask fits 4 (<= 128 VGPRs); the reset mask and fp32
 // z need more registers and run at 3; K = 32 at 2. The split form in 4-wave
 // blocks runs 3 blocks per CU (LDS), so 3 waves per SIMD.
-template <typename IoT, int K, bool RESET, int SPLIT = 1, int W = 8>
+template <typename IoT, int K, bool RESET, int W = 8, int RL = kRowLanes>
 constexpr int min_waves_per_simd() {
-  return K == 32 ? 2 : ((RESET || sizeof(IoT) == 4 || (SPLIT == 2 && W == 4)) ? 3 : 4);
+  return K == 32 ? 2 : ((RESET || sizeof(IoT) == 4 || (RL > kRowLanes && W == 4)) ? 3 : 4);
 }
 
 // The fused producer of x (nnterp "selective_scan" page, class docstring; the
@@ -148,59 +152,46 @@ __device__ __forceinline__ void conv_silu_lane(const IoT* __restrict__ xpg, int6
 // CW: 0, or the tap bound (4 or 8) of the fused causal conv1d + SiLU that
 // makes x from x_pre (p.x is then x_pre; see conv_silu_lane).
 //
-// SPLIT: 1, or 2 for the split form used when a launch has few rows (a wave
-// per SIMD or two): waves 2g and 2g + 1 share rows 4g..4g+3 of the block and
-// the chunk's B/C stage, and take state coordinates [0, N/2) and [N/2, N)
-// of every 16-coordinate group, so the launch has twice the waves for the
-// same rows. Each wave forms every token's step size (the exponents need all
-// of them), folds, scans and walks its own coordinates, and accumulates its
-// part of every token's y; the two parts meet in LDS once per chunk
-// (sYx, after a barrier), wave 2g finishing the first K/2 tokens of each
-// lane (D x, the gate, the store) and wave 2g + 1 the rest.
-template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0, int SPLIT = 1>
-__global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W>())) void scan_fwd_kernel(
+// RL: lanes per row, 16, or 32 / 64 for launches with few rows (a wave or
+// two per SIMD at 16): a row's chunk is then spread over 2 or 4 DPP rows,
+// the wave holds 2 rows or 1 and the launch twice or four times the waves;
+// the chunk scan takes one or two more steps across DPP rows, and B / C are
+// staged 8 or 4 coordinates at a time so that the stage stays 40 KB.
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0, int RL = kRowLanes>
+__global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>())) void scan_fwd_kernel(
     const ScanParams p) {
   static_assert(CW == 0 || (K == 16 && STATES == kNoStates), "the fused conv runs at 16 tokens per lane");
-  static_assert(SPLIT == 1 || (STATES == kNoStates && W % 2 == 0), "the split form writes y and h_last only");
-  using S = Shape<K, W, SPLIT>;
-  constexpr int KH = K / SPLIT;  // tokens per lane this wave finishes (y, gate, store)
-  // PF: the split form in 4-wave blocks (bf16, 3 waves per SIMD, registers
-  // to spare) loads the next chunk's x and dt and this chunk's z while it
-  // computes. (B and C of the next chunk as well, 16 more registers per
-  // lane, spilled and measured slower.)
-  constexpr bool PF = SPLIT == 2 && W == 4 && sizeof(IoT) == 2 && CW == 0 && !RESET;
+  static_assert(RL == kRowLanes || STATES == kNoStates, "long rows: y and h_last only");
+  using S = Shape<K, W, RL>;
+  constexpr int RPW = S::kRows;
   constexpr int T = S::kT;
   constexpr int KP = K + 4;  // LDS stride of one lane's K values (spreads the banks)
   constexpr int VEC = Io<IoT>::kVec;
   static_assert(K % VEC == 0 && K % 16 == 0, "K must hold whole 16-byte vectors");
   // State coordinates go in groups of NG: a group's B and C are staged in LDS
-  // at a time (one group when NMAX <= 16; LDS holds 16 coordinates' worth).
-  constexpr int NG = NMAX < 16 ? NMAX : 16;
+  // at a time (one group when NMAX <= 16 at 16 lanes per row; LDS holds 16
+  // coordinates' worth of 256-token chunks, 8 of 512, 4 of 1024).
+  constexpr int NGMAX = 16 * kRowLanes / RL;
+  constexpr int NG = NMAX < NGMAX ? NMAX : NGMAX;
   constexpr int kGroups = NMAX / NG;
   static_assert(kGroups * NG == NMAX, "NMAX is a multiple of the group size");
-  __shared__ float sB[NG][kRowLanes][KP];
-  __shared__ float sC[NG][kRowLanes][KP];
+  __shared__ float sB[NG][RL][KP];
+  __shared__ float sC[NG][RL][KP];
   __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
   __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
   __shared__ float sZero[NMAX];              // what lanes 1..15 read in place of the carry
-  // SPLIT: each wave's part of y for the K/2 tokens per lane its partner
-  // finishes, four tokens of a lane per float4, lanes adjacent (no bank
-  // conflicts)
-  __shared__ float4 sYx[SPLIT == 2 ? W : 1][SPLIT == 2 ? KH / 4 : 1][SPLIT == 2 ? 64 : 1];
   // kAllStates: one coordinate's states of the chunk per row, each lane's K
   // tokens padded to KP, re-read in token order for coalesced stores
   __shared__ __align__(16) float sSt[STATES == kAllStates ? S::kChan : 1][STATES == kAllStates ? kRowLanes * KP : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int gw = wave / SPLIT;    // the group of 4 rows this wave works on
-  const int half = wave % SPLIT;  // SPLIT: which half of the coordinates (and which tokens it finishes)
   const int lane = tid & 63;
-  const int row = lane >> 4;
-  const int tl = lane & 15;
+  const int row = lane / RL;
+  const int tl = lane % RL;
   const int64_t blk = blockIdx.x;
   const int64_t b = blk / p.chan_blocks;
-  const int64_t c_raw = (blk - b * p.chan_blocks) * S::kChan + gw * kRowsPerWave + row;
+  const int64_t c_raw = (blk - b * p.chan_blocks) * S::kChan + wave * RPW + row;
   const bool row_ok = c_raw < p.channels;
   const int64_t c = row_ok ? c_raw : p.channels - 1;  // rows past the end compute, never store
   const int N = p.N;
@@ -219,8 +210,8 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
   // row's slot; each 16-lane row only touches its own slot, and LDS accesses
   // of one wave complete in order, so no barrier guards them. Coordinates
   // n >= N get A2 = 0 and a zero state: they run as the identity.
-  const int slot = (gw * kRowsPerWave + row) * NMAX;
-  for (int n = tl; n < NMAX; n += kRowLanes) {
+  const int slot = (wave * RPW + row) * NMAX;
+  for (int n = tl; n < NMAX; n += RL) {
     sA2[slot + n] = n < N ? p.A[c * N + n] * kLog2e : 0.0f;
     sCarry[slot + n] = (n < N && p.h0) ? p.h0[(b * p.channels + c) * N + n] : 0.0f;
   }
@@ -229,29 +220,15 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
   // read zeros in its place, so the first fold step needs no select. sZero is
   // only ever read after the first chunk's staging barrier.
   const float* __restrict__ carry_src = tl == 0 ? &sCarry[slot] : sZero;
-  const bool carry_writer = tl == kRowLanes - 1;  // lane 15 ends the chunk
+  const bool carry_writer = tl == RL - 1;  // the row's last lane ends the chunk
   const float Dc = p.D ? p.D[c] : 0.0f;
   const float bias = p.dt_bias ? p.dt_bias[c] : 0.0f;
-
-  // PF: raw 16-byte vectors of this lane's x and dt in the next full chunk
-  uint4 px[PF ? K / VEC : 1], pd[PF ? K / VEC : 1];
-  auto prefetch = [&](int64_t t0n) {  // the chunk starting at t0n, which is full
-#pragma unroll
-    for (int v = 0; v < (PF ? K / VEC : 0); ++v) {
-      px[v] = *reinterpret_cast<const uint4*>(xg + t0n + tl * K + v * VEC);
-      pd[v] = *reinterpret_cast<const uint4*>(dg + t0n + tl * K + v * VEC);
-    }
-  };
-  if constexpr (PF) {
-    if (p.vec_ok && T <= L) prefetch(0);
-  }
 
   const int64_t nchunks = (L + T - 1) / T;
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     const int64_t t0 = ch * T;
     const int64_t tb = t0 + tl * K;  // this lane's first token
     const bool full = p.vec_ok && (t0 + T <= L);
-    const bool next_full = p.vec_ok && (t0 + 2 * T <= L);
 
     // 1. this lane's tokens of x and dt. z is loaded after the state loop:
     // held in registers across the loop it costs registers the loop needs
@@ -263,13 +240,8 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
     if (full) {
 #pragma unroll
       for (int v = 0; v < K / VEC; ++v) {
-        if constexpr (PF) {
-          unpack_vec16<IoT>(px[v], xv + v * VEC);
-          unpack_vec16<IoT>(pd[v], dv + v * VEC);
-        } else {
-          if constexpr (CW == 0) load_vec16(xg + tb + v * VEC, xv + v * VEC);
-          load_vec16(dg + tb + v * VEC, dv + v * VEC);
-        }
+        if constexpr (CW == 0) load_vec16(xg + tb + v * VEC, xv + v * VEC);
+        load_vec16(dg + tb + v * VEC, dv + v * VEC);
       }
     } else {
 #pragma unroll
@@ -355,19 +327,6 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
       __syncthreads();
     };
     stage(0);
-    // PF: this chunk's z (the tokens this wave finishes), then the next
-    // chunk's inputs, in flight during the state loop
-    uint4 pz[PF && GATE ? KH / VEC : 1];
-    if constexpr (PF && GATE) {
-      if (full) {
-#pragma unroll
-        for (int v = 0; v < KH / VEC; ++v)
-          pz[v] = *reinterpret_cast<const uint4*>(zg + tb + half * KH + v * VEC);
-      }
-    }
-    if constexpr (PF) {
-      if (next_full) prefetch(t0 + T);
-    }
 
     // 3. per-token step size, dt*x, skip term
     float dtv[K], dtx[K], yv[K], mj[RESET ? K : 1];
@@ -388,9 +347,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
     for (int j = 0; j < K; ++j) {
       const float d = dtv[j];
       dtx[j] = d * xv[j];
-      // (SPLIT: D x only in the part of the wave that finishes the token;
-      // then x is dead during the state loop)
-      yv[j] = (SPLIT == 1 || (j < KH) == (half == 0)) ? Dc * xv[j] : 0.0f;
+      yv[j] = Dc * xv[j];
       sdt += d;
       if constexpr (RESET) {
         const bool r = (rbits >> j) & 1u;
@@ -408,10 +365,8 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
       jsel = (jd >= 0 && jd < K) ? (int)jd : -1;
     }
     auto coords = [&](int grp) {
-      constexpr int NGH = NG / SPLIT;  // coordinates of the group this wave takes
 #pragma unroll
-      for (int i = 0; i < NGH; ++i) {
-        const int nl = half * NGH + i;
+      for (int nl = 0; nl < NG; ++nl) {
         const int n = grp * NG + nl;
         const float a2n = sA2[slot + n];
         const float carry_l = carry_src[n];
@@ -435,7 +390,7 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
 #pragma unroll
         for (int j = 1; j < K; ++j) Bl = __builtin_fmaf(av[j], Bl, bv[j]);
         float h = f0;
-        row16_scan_and_enter(Al, Bl, h, av[0]);  // Bl: state after this lane's tokens; h: after its first
+        row_scan_and_enter<RL>(Al, Bl, h, av[0]);  // Bl: state after this lane's tokens; h: after its first
         if (carry_writer) sCarry[slot + n] = Bl;  // state after the chunk (in place)
         float hsel = 0.0f;  // kOneState: the state after the selected token
 #pragma unroll
@@ -497,81 +452,45 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, SPLIT, W
       coords(grp);
     }
 
-    // 5. (SPLIT) the two waves' parts of y meet: each hands over the part
-    // for the tokens its partner finishes and adds the partner's part to its
-    // own. (Waves reach the next write of sYx only after the
-    // next chunk's first staging barrier, so one barrier per chunk does.)
-    float yo[KH];  // y of the tokens this wave finishes, tb + half * KH + i
-    if constexpr (SPLIT == 2) {
-      // (selects on the wave-uniform half, with constant register indexes)
-      float ymine[KH], ygive[KH];
-#pragma unroll
-      for (int i = 0; i < KH; ++i) {
-        ymine[i] = half ? yv[KH + i] : yv[i];
-        ygive[i] = half ? yv[i] : yv[KH + i];
-      }
-#pragma unroll
-      for (int q = 0; q < KH / 4; ++q)
-        sYx[wave][q][lane] = make_float4(ygive[4 * q], ygive[4 * q + 1], ygive[4 * q + 2], ygive[4 * q + 3]);
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < KH / 4; ++q) {
-        const float4 o = sYx[wave ^ 1][q][lane];
-        const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yo[4 * q + i] = ymine[4 * q + i] + ov[i];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < K; ++j) yo[j] = yv[j];
-    }
-
-    // 6. gate and store
-    const int64_t to = tb + half * KH;
+    // 5. gate and store
     if constexpr (GATE) {
-      float zv[KH];
+      float zv[K];
       if (full) {
 #pragma unroll
-        for (int v = 0; v < KH / VEC; ++v) {
-          if constexpr (PF) unpack_vec16<IoT>(pz[v], zv + v * VEC);
-          else load_vec16(zg + to + v * VEC, zv + v * VEC);
-        }
+        for (int v = 0; v < K / VEC; ++v) load_vec16(zg + tb + v * VEC, zv + v * VEC);
       } else {
 #pragma unroll
-        for (int j = 0; j < KH; ++j) zv[j] = to + j < L ? Io<IoT>::to_f32(zg[to + j]) : 0.0f;
+        for (int j = 0; j < K; ++j) zv[j] = tb + j < L ? Io<IoT>::to_f32(zg[tb + j]) : 0.0f;
       }
 #pragma unroll
-      for (int j = 0; j < KH; ++j) yo[j] *= silu_f32(zv[j]);
+      for (int j = 0; j < K; ++j) yv[j] *= silu_f32(zv[j]);
     }
     if (row_ok) {
       if (full) {
 #pragma unroll
-        for (int v = 0; v < KH / VEC; ++v) store_vec16(yg + to + v * VEC, yo + v * VEC);
+        for (int v = 0; v < K / VEC; ++v) store_vec16(yg + tb + v * VEC, yv + v * VEC);
       } else {
 #pragma unroll
-        for (int j = 0; j < KH; ++j)
-          if (to + j < L) yg[to + j] = Io<IoT>::from_f32(yo[j]);
+        for (int j = 0; j < K; ++j)
+          if (tb + j < L) yg[tb + j] = Io<IoT>::from_f32(yv[j]);
       }
     }
   }
 
-  // (SPLIT: each wave writes the coordinates it carried; its own LDS writes
-  // of sCarry are complete in order, so no barrier is needed)
   if (p.h_last && row_ok)
-    for (int n = tl; n < N; n += kRowLanes)
-      if (SPLIT == 1 || (n % NG) / (NG / SPLIT) == half) p.h_last[(b * p.channels + c) * N + n] = sCarry[slot + n];
+    for (int n = tl; n < N; n += RL) p.h_last[(b * p.channels + c) * N + n] = sCarry[slot + n];
 }
 
-template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0, int SPLIT = 1>
+template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0, int RL = kRowLanes>
 hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
-  using S = Shape<K, W, SPLIT>;
+  using S = Shape<K, W, RL>;
   ScanParams p = p0;
   p.chan_blocks = (p.channels + S::kChan - 1) / S::kChan;
   const int64_t blocks = p.batch * p.chan_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {&p};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES, CW, SPLIT>),
+      reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES, CW, RL>),
       dim3((unsigned)blocks), dim3(S::kThreads), args, 0, stream);
 }
 
@@ -585,21 +504,23 @@ hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
 // two sets in separate files, each built with the machine scheduler that
 // measured faster for it.
 //
-// split (0, 4 or 8): the split form in blocks of that many waves, for a
-// launch without a reset mask at K = 16 and N <= 16 (where it is
-// instantiated); 0 = the plain form. The caller picks it (split_waves).
+// form: how a launch with few rows spreads them, for a launch without a
+// reset mask at K = 16 and N <= 16 (where the forms are instantiated):
+// kPlain, or kRows32w4 / kRows32w8 / kRows64w4: rows of 32 or 64 lanes in
+// blocks of 4 or 8 waves. The caller picks it.
 template <typename IoT, int K, int NMAX, int STATES, int RESETS, int CW = 0>
-hipError_t launch_flags(const ScanParams& p, hipStream_t stream, int split = 0) {
+hipError_t launch_flags(const ScanParams& p, hipStream_t stream, int form = 0) {
   const bool gate = p.z != nullptr, reset = p.reset != nullptr;
   if constexpr (K == 16 && NMAX <= 16 && STATES == kNoStates && RESETS == 0 && CW == 0) {
-    if (split == 4) {
-      if (gate) return launch_t<IoT, K, 4, NMAX, true, false, STATES, CW, 2>(p, stream);
-      return launch_t<IoT, K, 4, NMAX, false, false, STATES, CW, 2>(p, stream);
-    }
-    if (split == 8) {
-      if (gate) return launch_t<IoT, K, 8, NMAX, true, false, STATES, CW, 2>(p, stream);
-      return launch_t<IoT, K, 8, NMAX, false, false, STATES, CW, 2>(p, stream);
-    }
+#define SS_FORM(CODE, WV, RLN)                                                         \
+  if (form == CODE) {                                                                  \
+    if (gate) return launch_t<IoT, K, WV, NMAX, true, false, STATES, CW, RLN>(p, stream); \
+    return launch_t<IoT, K, WV, NMAX, false, false, STATES, CW, RLN>(p, stream);         \
+  }
+    SS_FORM(kRows32w4, 4, 32)
+    SS_FORM(kRows32w8, 8, 32)
+    SS_FORM(kRows64w4, 4, 64)
+#undef SS_FORM
   }
   // 8-wave blocks when 4 waves fit per SIMD (two blocks per CU), else 4-wave
   // blocks (three per CU at 3 waves per SIMD)
@@ -623,10 +544,10 @@ hipError_t launch_flags(const ScanParams& p, hipStream_t stream, int split = 0) 
 // N_max instances: 4, 8, 16, 32, 64 (coordinates past N run as the identity).
 // K = 32 is instantiated up to 16 coordinates only; wider states take K = 16.
 template <typename IoT, int K, int STATES, int RESETS>
-hipError_t launch_n(const ScanParams& p, hipStream_t stream, int split = 0) {
-  if (p.N <= 4) return launch_flags<IoT, K, 4, STATES, RESETS>(p, stream, split);
-  if (p.N <= 8) return launch_flags<IoT, K, 8, STATES, RESETS>(p, stream, split);
-  if (p.N <= 16) return launch_flags<IoT, K, 16, STATES, RESETS>(p, stream, split);
+hipError_t launch_n(const ScanParams& p, hipStream_t stream, int form = 0) {
+  if (p.N <= 4) return launch_flags<IoT, K, 4, STATES, RESETS>(p, stream, form);
+  if (p.N <= 8) return launch_flags<IoT, K, 8, STATES, RESETS>(p, stream, form);
+  if (p.N <= 16) return launch_flags<IoT, K, 16, STATES, RESETS>(p, stream, form);
   if constexpr (K == 16) {
     if (p.N <= 32) return launch_flags<IoT, K, 32, STATES, RESETS>(p, stream);
     return launch_flags<IoT, K, 64, STATES, RESETS>(p, stream);

@@ -45,27 +45,32 @@ int pick_k(const ScanParams& p) {
   return (p.reset != nullptr && p.L >= 8192 && blocks <= 2 * static_cast<int64_t>(device_cus())) ? 32 : 16;
 }
 
-// The split form (two waves per group of 4 rows, each on half of the state
-// coordinates) for launches whose plain grid would give each SIMD at most
-// about two waves: there a wave's dependent chains leave the SIMD idle
-// between issues and the work does not spread evenly (6144 rows are 1536
-// waves on 1024 SIMDs). Returns the split block's waves: 4 when its blocks
-// (8 rows, about 50 KB of LDS) fit one round of 3 per CU, 8 when 16-row
-// blocks fit one round of 2 per CU, else 0 (the plain form). Only for K = 16
-// without a reset mask and N <= 16. SS_SCAN_SPLIT=off, =4 or =8 (read at
-// every call) overrides the rule.
-int split_waves(const ScanParams& p) {
-  if (p.N > 16) return 0;
+// The launch form for few rows (scan_chunked.h, Form): rows of 32 or 64
+// lanes (a wave on 2 channels or 1), for launches whose plain grid would give
+// each SIMD at most about two waves: there a wave's dependent chains leave
+// the SIMD idle between issues, and the work does not spread evenly (6144
+// rows are 1536 waves on 1024 SIMDs). The form is the first whose grid fits
+// one round: 64-lane rows in 4-wave blocks (3 per CU, by LDS), 32-lane rows
+// in 4-wave blocks, 32-lane rows in 8-wave blocks (2 per CU). Measured on
+// MI355X, bf16 with gate, seq 2048: 4 x 1536 channels 82.7 -> 61.7 us
+// (32 lanes, 4 waves; 64 lanes: 67.5); 1 x 3072: 80.7 -> 39.8 (64 lanes);
+// 2 x 2048: 81.8 -> 49.1 (32 lanes, 4 waves); 4 x 2048: 85.9 -> 77.9 (32
+// lanes, 8 waves). Only for K = 16 without a reset mask and N <= 16. SS_SCAN_SPLIT=off, =r32w4, =r32w8 or =r64w4 (read at every
+// call) overrides the rule.
+int few_rows_form(const ScanParams& p) {
+  if (p.N > 16) return kPlain;
   if (const char* e = std::getenv("SS_SCAN_SPLIT")) {
     const std::string v(e);
-    if (v == "off") return 0;
-    if (v == "4") return 4;
-    if (v == "8") return 8;
+    if (v == "off") return kPlain;
+    if (v == "r32w4") return kRows32w4;
+    if (v == "r32w8") return kRows32w8;
+    if (v == "r64w4") return kRows64w4;
   }
   const int64_t cus = device_cus();
-  if (p.batch * ((p.channels + 7) / 8) <= 3 * cus) return 4;
-  if (p.batch * ((p.channels + 15) / 16) <= 2 * cus) return 8;
-  return 0;
+  if (p.batch * ((p.channels + 3) / 4) <= 3 * cus) return kRows64w4;  // 4-wave blocks, 3 per CU
+  if (p.batch * ((p.channels + 7) / 8) <= 3 * cus) return kRows32w4;
+  if (p.batch * ((p.channels + 15) / 16) <= 2 * cus) return kRows32w8;  // 8-wave blocks, 2 per CU
+  return kPlain;
 }
 
 // 1 = row-parallel walk, 2 = chunked scan. The chunked scan is the default:
@@ -86,11 +91,11 @@ hipError_t launch_scan_fwd(const ScanParams& p, bool io_bf16, hipStream_t stream
   if (pick_kernel(p, io_bf16) == 1) return launch_scan_rows(p, io_bf16, stream);
   const int K = pick_k(p);
   if (p.reset) return launch_scan_fwd_reset(p, io_bf16, K, stream);
-  const int split = K == 16 ? split_waves(p) : 0;
+  const int form = K == 16 ? few_rows_form(p) : kPlain;
   if (io_bf16)
     return K == 32 ? launch_n<bf16_t, 32, kNoStates, 0>(p, stream)
-                   : launch_n<bf16_t, 16, kNoStates, 0>(p, stream, split);
-  return K == 32 ? launch_n<float, 32, kNoStates, 0>(p, stream) : launch_n<float, 16, kNoStates, 0>(p, stream, split);
+                   : launch_n<bf16_t, 16, kNoStates, 0>(p, stream, form);
+  return K == 32 ? launch_n<float, 32, kNoStates, 0>(p, stream) : launch_n<float, 16, kNoStates, 0>(p, stream, form);
 }
 
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels) {

@@ -184,4 +184,70 @@ __device__ __forceinline__ void row16_scan_and_enter(float A, float& B, float& h
       : "v"(a0));
 }
 
+// The same over 32-lane segments (lanes 0..31 and 32..63): the 16-lane scan
+// with the A products completed, then one step in which rows 1 and 3 combine
+// with lane 15 of the row before (row_bcast:15, rows 0 and 2 masked off).
+// The entry: lanes 1..31 of the first segment and 16..31 of the second take
+// lane l-1 through a wave-wide shift (wave_shr:1, row 2 masked off: its first
+// lane starts the second segment), lanes 33..47 through row_shr:1 on row 2
+// alone; lanes 0 and 32 keep h.
+__device__ __forceinline__ void row32_scan_and_enter(float A, float& B, float& h, float a0) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %2, %1, %3 wave_shr:1 row_mask:0xb bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %1, %3 row_shr:1 row_mask:0x4 bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B), "+v"(h)
+      : "v"(a0));
+}
+
+// Over the whole wave (64 lanes): the 32-lane steps with the A products of
+// rows 1 and 3 completed, then rows 2 and 3 combine with lane 31
+// (row_bcast:31); the entry shifts across the wave (lane 0 keeps h).
+__device__ __forceinline__ void row64_scan_and_enter(float A, float& B, float& h, float a0) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %2, %1, %3 wave_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      : "+v"(A), "+v"(B), "+v"(h)
+      : "v"(a0));
+}
+
+template <int RL>
+__device__ __forceinline__ void row_scan_and_enter(float A, float& B, float& h, float a0) {
+  static_assert(RL == 16 || RL == 32 || RL == 64, "segments of 16, 32 or 64 lanes");
+  if constexpr (RL == 16) row16_scan_and_enter(A, B, h, a0);
+  else if constexpr (RL == 32) row32_scan_and_enter(A, B, h, a0);
+  else row64_scan_and_enter(A, B, h, a0);
+}
+
 }  // namespace ss

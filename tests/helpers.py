@@ -82,17 +82,18 @@ def to_dev(inp, device="cuda"):
 
 
 # The prompt-scan kernel variants the GPU tests run: the chunked scan at 16
-# and at 32 tokens per lane, its split form (two waves per group of rows,
-# each on half of the state coordinates) in 4- and 8-wave blocks, and the
-# row-parallel walk. The library picks one by shape; SS_SCAN_KERNEL,
+# and at 32 tokens per lane; its forms for few rows at 16 tokens per lane,
+# rows of 32 lanes (4- and 8-wave blocks) or 64 lanes; and the row-parallel
+# walk. The library picks one by shape; SS_SCAN_KERNEL,
 # SS_SCAN_TOKENS_PER_LANE and SS_SCAN_SPLIT, read at every call, force one.
-# (The split form takes no reset mask: with one, the split variants run the
+# (The few-row forms take no reset mask and N <= 16: past that, they run the
 # plain chunked scan.)
-SCAN_KERNELS = ["chunked", "chunked32", "split4", "split8", "rows"]
+_FORMS = {"rows32": "r32w4", "rows32w8": "r32w8", "rows64": "r64w4"}
+SCAN_KERNELS = ["chunked", "chunked32", *_FORMS, "rows"]
 RESET_SCAN_KERNELS = ["chunked", "chunked32", "rows"]
 
 
 def force_scan_kernel(monkeypatch, kind):
     monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if kind == "rows" else "chunked")
     monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if kind == "chunked32" else "16")
-    monkeypatch.setenv("SS_SCAN_SPLIT", kind[len("split"):] if kind.startswith("split") else "off")
+    monkeypatch.setenv("SS_SCAN_SPLIT", _FORMS.get(kind, "off"))

@@ -309,16 +309,16 @@ def test_decode_shapes(io, N, gate):
     check_close(np64(state), sr, *TOL_STATE, "decode state")
 
 
-@pytest.mark.parametrize("split", ["4", "8"])
+@pytest.mark.parametrize("form", ["rows32", "rows32w8", "rows64"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 9, 12, 16, 17])
-def test_split_form_state_dims(N, io, split, monkeypatch):
-    """The split form (each of two waves on half of a row group's state
-    coordinates, y summed through LDS) at every instantiated state width, a
-    ragged channel count (21: partial 8- and 16-row blocks) and a ragged tail
-    over several chunks; N = 17 is past the split form's range and takes the
-    plain scan."""
-    force_scan_kernel(monkeypatch, "split" + split)
-    print(f"split form {split} waves io={io} N={N}", flush=True)
-    inp = make_case(330 + N, 2, 21, N, 777, io, gate=N % 2 == 0, h0=N % 3 != 0)
-    compare_full(inp, what=f"split{split} {io} N={N}")
+def test_few_row_forms_state_dims(N, io, form, monkeypatch):
+    """The forms for few rows (rows of 32 and 64 lanes: the chunk scan over 2
+    and 4 DPP rows, B/C staged in 8- and 4-coordinate groups) at every
+    instantiated state width, a ragged channel count (21: partial blocks) and
+    a ragged tail over several chunks of 512 and 1024 tokens; N = 17 is past
+    their range and takes the plain scan."""
+    force_scan_kernel(monkeypatch, form)
+    print(f"few-row form {form} io={io} N={N}", flush=True)
+    inp = make_case(330 + N, 2, 21, N, 2777, io, gate=N % 2 == 0, h0=N % 3 != 0)
+    compare_full(inp, what=f"{form} {io} N={N}")

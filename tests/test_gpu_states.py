@@ -4,7 +4,10 @@ state_dim, seq], the oracle's [.., seq, state_dim] transposed) and after one
 selected token
 (TransformerLens "ssm_mixer" page, compute_ssm_state(time_step)) against the
 fp64 oracle's per-token states; y and h_last are bitwise those of
-ss_scan_fwd.
+ss_scan_fwd in its plain chunked form (the same kernel with the state
+output switched off; the forms for few rows, which ss_scan_fwd picks at
+these small shapes, combine in another order, so the module forces the plain
+form through SS_SCAN_SPLIT=off).
 
 The states are fp32 for every I/O type and are held to the fp32 bar."""
 import pytest
@@ -16,6 +19,11 @@ from selective_state_space_ss_amd.workloads import make_case
 from tests.helpers import TOL_STATE, check_close, np64, to_dev
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def plain_scan_form(monkeypatch):
+    monkeypatch.setenv("SS_SCAN_SPLIT", "off")
 
 
 def oracle_states(inp):
