@@ -255,9 +255,15 @@ template <typename IoT, int KCH>
 struct ProjTileLds {
   static constexpr int E = 16 / sizeof(IoT);
   static constexpr int DP = KCH * 4 * E + E;       // delta row pitch (elements), padded by one vector
-  static constexpr int OP = kProjStepT + E;        // output row pitch
+  // The output tile's rows are 64 tokens (8 or 16 vectors of 16 bytes), with
+  // vector j of row r stored at position j ^ swz(r): the MFMA results of 16
+  // (or 32) channels going in at the same token, and the 16-lane runs of a
+  // row coming out, then touch every bank once.
+  static constexpr int OV = kProjStepT / E;        // 16-byte vectors per output row
+  __device__ static int swz(int r) { return E == 8 ? (r >> 1) & 7 : r & 15; }
+  __device__ static int opos(int r, int t) { return ((t / E) ^ swz(r)) * E + t % E; }  // t: token in the row
   IoT d[2][kProjStepT][DP];
-  IoT o[kProjWaves][kProjWaveC][OP];
+  IoT o[kProjWaves][kProjWaveC][kProjStepT];
 };
 
 template <typename IoT, int KCH>
@@ -276,7 +282,7 @@ void dt_proj_tile_kernel(const ProjParams p) {
   constexpr int kThreads = 64 * kProjWaves;
   constexpr int TV = kProjStepT * RV;              // vectors per delta tile
   constexpr int NPF = (TV + kThreads - 1) / kThreads;
-  constexpr int OV = kProjStepT / E;               // 16-byte vectors per output row
+  constexpr int OV = Lds::OV;
   __shared__ __align__(16) Lds st;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, G = l >> 4, r16 = l & 15;
@@ -290,12 +296,32 @@ void dt_proj_tile_kernel(const ProjParams p) {
   const IoT* __restrict__ Dall = static_cast<const IoT*>(p.delta);
   IoT* __restrict__ Oall = static_cast<IoT*>(p.dt);
 
-  // block-cooperative delta tile of unit u, through registers
+  // A unit's place: batch row b, channel group g, token step s (tokens
+  // inner). The block walks its units in order, so places advance by one
+  // step at a time (no divisions past the first).
+  struct Place {
+    int64_t b, g, s;
+  };
+  auto place_of = [&](int64_t u) {
+    const int64_t bg = u / nsteps;
+    return Place{bg / groups, bg % groups, u - bg * nsteps};
+  };
+  auto next_place = [&](Place q) {
+    if (++q.s == nsteps) {
+      q.s = 0;
+      if (++q.g == groups) {
+        q.g = 0;
+        ++q.b;
+      }
+    }
+    return q;
+  };
+
+  // block-cooperative delta tile of a unit, through registers
   u32x4 pf[NPF];
-  auto fetch = [&](int64_t u) {
-    const int64_t bg = u / nsteps, b = bg / groups;
-    const int64_t t0 = (u - bg * nsteps) * kProjStepT;
-    const IoT* D = Dall + b * L * R;
+  auto fetch = [&](Place q) {
+    const int64_t t0 = q.s * kProjStepT;
+    const IoT* D = Dall + q.b * L * R;
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
       const int e = tid + n * kThreads;
@@ -315,9 +341,14 @@ void dt_proj_tile_kernel(const ProjParams p) {
     }
   };
 
-  fetch(u0);
+  Place cur = place_of(u0);  // the unit being computed
+  Place ahead = cur;         // the unit whose tile is in pf
+  fetch(ahead);
   stash(0);
-  if (u0 + 1 < u1) fetch(u0 + 1);
+  if (u0 + 1 < u1) {
+    ahead = next_place(ahead);
+    fetch(ahead);
+  }
 
   u32x4 wf[2][KCH];
   float bias[2] = {0.0f, 0.0f};
@@ -328,10 +359,14 @@ void dt_proj_tile_kernel(const ProjParams p) {
     __syncthreads();
     if (u + 1 < u1) {
       stash(buf ^ 1);
-      if (u + 2 < u1) fetch(u + 2);
+      if (u + 2 < u1) {
+        ahead = next_place(ahead);
+        fetch(ahead);
+      }
     }
-    const int64_t bg = u / nsteps, b = bg / groups, g = bg - b * groups;
-    const int64_t t0 = (u - bg * nsteps) * kProjStepT;
+    if (u > u0) cur = next_place(cur);
+    const int64_t b = cur.b, g = cur.g, bg = b * groups + g;
+    const int64_t t0 = cur.s * kProjStepT;
     const int64_t c0 = g * kProjGroupC + w * kProjWaveC;  // this wave's 32 channels
     if (bg != wbg) {
       // B operands of column tile m: lane (r16, G) holds w_dt[c0 + 16 m + r16][kc KC + E G ..]
@@ -352,7 +387,9 @@ void dt_proj_tile_kernel(const ProjParams p) {
       u32x4 af[KCH];
 #pragma unroll
       for (int kc = 0; kc < KCH; ++kc) af[kc] = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * q + r16][kc * KC + E * G]);
-      v4f acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+      // (the accumulators start from the bias: every register of a lane is
+      // one channel, so dt + dt_bias costs no add)
+      v4f acc[2] = {{bias[0], bias[0], bias[0], bias[0]}, {bias[1], bias[1], bias[1], bias[1]}};
 #pragma unroll
       for (int kc = 0; kc < KCH; ++kc) {
 #pragma unroll
@@ -376,8 +413,8 @@ void dt_proj_tile_kernel(const ProjParams p) {
       for (int m = 0; m < 2; ++m) {
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = APPLY ? softplus_f32(acc[m][r] + bias[m]) : acc[m][r];
-        IoT* dst = &st.o[w][16 * m + r16][16 * q + 4 * G];
+        for (int r = 0; r < 4; ++r) v[r] = APPLY ? softplus_f32(acc[m][r]) : acc[m][r];
+        IoT* dst = &st.o[w][16 * m + r16][Lds::opos(16 * m + r16, 16 * q + 4 * G)];
         if constexpr (sizeof(IoT) == 2) {
           const uint32_t lo = pack_bf16x2(v[0], v[1]);
           const uint32_t hi = pack_bf16x2(v[2], v[3]);
@@ -396,7 +433,7 @@ void dt_proj_tile_kernel(const ProjParams p) {
       const int row = e / OV, tv = (e - row * OV) * E;
       const int64_t c = c0 + row, t = t0 + tv;
       if (c < C && t < L)  // L is a whole number of 16-byte vectors
-        stream_store16(*reinterpret_cast<const uint4*>(&st.o[w][row][tv]), out + c * L + t);
+        stream_store16(*reinterpret_cast<const uint4*>(&st.o[w][row][Lds::opos(row, tv)]), out + c * L + t);
     }
   }
 }
