@@ -131,6 +131,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle sample")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
+    ap.add_argument("--counter-workload", metavar="NAME",
+                    help="with --counter-pass: run 3 launches of that configuration's scan (tiny_fp32, mamba130m, "
+                         "packed_reset, mamba2p8b) instead of the steps")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes into " + TRAFFIC_FILE)
     ap.add_argument("--summarize-trace", metavar="KT_DIR",
@@ -138,6 +141,11 @@ def parse():
                          "launch shape (grid x block), and exit")
     ap.add_argument("--probe-issue", metavar="OUT_JSON",
                     help="run the fp32 FMA / transcendental issue-rate probe, write its JSON to OUT_JSON, exit")
+    ap.add_argument("--probe-lds", action="store_true",
+                    help="launch the LDS bank probe once per offset pattern (for a rocprofv3 --pmc "
+                         "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS pass), print the pattern names as JSON, exit")
+    ap.add_argument("--summarize-lds", metavar="PMC_DIR",
+                    help="print a markdown table of conflict cycles per instruction from a --probe-lds pass, exit")
     return ap.parse_args()
 
 
@@ -631,8 +639,95 @@ def cpu_baseline(inp, w, budget_s: float):
     }
 
 
+# LDS bank probe (libssprobe.so ssprobe_lds): (name, access bytes, write?,
+# byte offset of each of the 64 lanes). The first launch warms up and is not
+# a pattern.
+LDS_PROBE_ITERS = 1000
+
+
+def lds_patterns():
+    L = range(64)
+    pats = [
+        ("read b128, lanes contiguous", 16, 0, [16 * l for l in L]),
+        ("read b128, every lane one address", 16, 0, [0] * 64),
+        ("read b128, lane stride 32 B", 16, 0, [32 * l for l in L]),
+        ("read b128, lane stride 64 B", 16, 0, [64 * l for l in L]),
+        ("read b128, lane stride 256 B", 16, 0, [256 * l for l in L]),
+        ("read b128, 16 lanes contiguous, 4 rows alike", 16, 0, [16 * (l % 16) for l in L]),
+        ("read b128, 16 lanes contiguous, rows 256 B apart", 16, 0, [16 * (l % 16) + 256 * (l // 16) for l in L]),
+        ("read b128, scan B/C: lane stride 80 B, 4 rows alike", 16, 0, [80 * (l % 16) for l in L]),
+        ("read b128, lane stride 64 B, 4 rows alike", 16, 0, [64 * (l % 16) for l in L]),
+        ("read b128, dt_proj delta: lane stride 336 B, rows +16 B", 16, 0,
+         [336 * (l % 16) + 16 * (l // 16) for l in L]),
+        ("read b128, lane stride 336 B, 4 rows alike", 16, 0, [336 * (l % 16) for l in L]),
+        ("read b128, lane stride 80 B, rows +16 B", 16, 0, [80 * (l % 16) + 16 * (l // 16) for l in L]),
+        ("read b64, lanes contiguous", 8, 0, [8 * l for l in L]),
+        ("read b64, lane stride 16 B", 8, 0, [16 * l for l in L]),
+        ("read b32, lanes contiguous", 4, 0, [4 * l for l in L]),
+        ("read b32, lane stride 8 B", 4, 0, [8 * l for l in L]),
+        ("write b128, lanes contiguous", 16, 1, [16 * l for l in L]),
+        ("write b128, lane stride 32 B", 16, 1, [32 * l for l in L]),
+        ("write b128, scan B/C staging (bf16, 16 tokens per lane)", 16, 1,
+         [4 * (((l % 32) // 2) * 20 + 8 * (l % 2)) + 4 * 320 * (l // 32) for l in L]),
+        ("write b64, lanes contiguous", 8, 1, [8 * l for l in L]),
+        ("write b64, lane stride 16 B", 8, 1, [16 * l for l in L]),
+        ("write b32, lanes contiguous", 4, 1, [4 * l for l in L]),
+    ]
+    for name, width, _, offs in pats:
+        assert len(offs) == 64 and all(0 <= o <= 65536 - 16 and o % width == 0 for o in offs), name
+    return pats
+
+
+def probe_lds():
+    import ctypes
+    import torch
+    from selective_state_space_ss_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.ssprobe_lds.restype = ctypes.c_int
+    lib.ssprobe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    pats = lds_patterns()
+    out = torch.empty(64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    offs = [torch.tensor(o, dtype=torch.int32, device="cuda") for _, _, _, o in pats]
+    for k, (name, width, write, _) in enumerate([pats[0]] + pats):
+        t = offs[max(k - 1, 0)]
+        if lib.ssprobe_lds(t.data_ptr(), width, LDS_PROBE_ITERS, write, out.data_ptr(), stream) != 0:
+            raise RuntimeError(f"ssprobe_lds failed on {name}")
+    torch.cuda.synchronize()
+    print(json.dumps([p[0] for p in pats]), flush=True)
+
+
+def summarize_lds(pmc_dir: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "lds_probe_kernel" not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[1:]  # the first launch is the warm-up
+    pats = lds_patterns()
+    if len(ids) != len(pats):
+        raise SystemExit(f"expected {len(pats)} probe launches after the warm-up, found {len(ids)}")
+    print("| pattern | bytes per lane | conflict cycles per instruction |")
+    print("|---|---|---|")
+    for (name, width, _, _), i in zip(pats, ids):
+        c = per[i]
+        print(f"| {name} | {width} | {c.get('SQ_LDS_BANK_CONFLICT', 0.0) / LDS_PROBE_ITERS:.2f} |")
+
+
 def main():
     args = parse()
+    if args.summarize_lds:
+        summarize_lds(args.summarize_lds)
+        return
+    if args.probe_lds:
+        probe_lds()
+        return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
@@ -685,8 +780,14 @@ def main():
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
-        for _ in range(3):
-            step()
+        if args.counter_workload:
+            c = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(args.counter_workload).items()}
+            for _ in range(3):
+                ss.ss_scan_fwd(c["x"], c["dt"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"], dt_bias=c["dt_bias"],
+                               h0=c["h0"], reset=c["reset"])
+        else:
+            for _ in range(3):
+                step()
         torch.cuda.synchronize()
         print("counter pass done", flush=True)
         return

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssscan.so")
 # measurement support for bench.py (issue-rate probe), kept out of the scan's library
 PROBE_LIB = os.path.join(PKG, "libssprobe.so")
-PROBE_SOURCES = ["probe_issue.hip"]
+PROBE_SOURCES = ["probe_issue.hip", "probe_lds.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_fwd_reset.hip", "scan_fwd_conv.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
