@@ -254,7 +254,7 @@ constexpr int kProjStepT = 64;                     // tokens per unit (four MFMA
 template <typename IoT, int KCH>
 struct ProjTileLds {
   static constexpr int E = 16 / sizeof(IoT);
-  static constexpr int DP = KCH * 4 * E + E;       // delta row pitch (elements), padded by one vector
+  static constexpr int NCH = KCH * 4;              // 16-byte pieces of k per delta row
   // The output tile's rows are 64 tokens (8 or 16 vectors of 16 bytes), with
   // vector j of row r stored at position j ^ swz(r): the MFMA results of 16
   // (or 32) channels going in at the same token, and the 16-lane runs of a
@@ -262,7 +262,12 @@ struct ProjTileLds {
   static constexpr int OV = kProjStepT / E;        // 16-byte vectors per output row
   __device__ static int swz(int r) { return E == 8 ? (r >> 1) & 7 : r & 15; }
   __device__ static int opos(int r, int t) { return ((t / E) ^ swz(r)) * E + t % E; }  // t: token in the row
-  IoT d[2][kProjStepT][DP];
+  // The delta tile piece by piece: piece j (k = jE .. jE + E - 1) of every
+  // token, tokens adjacent. A 16-lane quarter of an operand read then takes
+  // 256 contiguous bytes, and the four quarters (one piece each) are 1 KiB
+  // apart; rows of the tile with the pieces adjacent would put the quarters
+  // 16 bytes apart, which the LDS serves with a conflict cycle per quarter.
+  IoT d[2][NCH][kProjStepT][E];
   IoT o[kProjWaves][kProjWaveC][kProjStepT];
 };
 
@@ -317,15 +322,26 @@ void dt_proj_tile_kernel(const ProjParams p) {
     return q;
   };
 
-  // block-cooperative delta tile of a unit, through registers
+  // block-cooperative delta tile of a unit, through registers. Thread
+  // piece e covers token t and 16-byte piece j of k: runs of 8 threads take
+  // 8 consecutive tokens of one piece (so an 8-lane LDS store group writes
+  // 128 contiguous bytes), and a wave's 64 threads 8 tokens x 8 pieces
+  // (128 contiguous bytes of each token's row in memory).
   u32x4 pf[NPF];
+  auto piece = [&](int e, int& t, int& j) {
+    const int f = e % (8 * RV);
+    t = (e / (8 * RV)) * 8 + (f & 7);
+    j = f >> 3;
+  };
   auto fetch = [&](Place q) {
     const int64_t t0 = q.s * kProjStepT;
     const IoT* D = Dall + q.b * L * R;
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
       const int e = tid + n * kThreads;
-      const int t = e / RV, kv = (e - t * RV) * E;
+      int t, j;
+      piece(e, t, j);
+      const int kv = j * E;
       const bool in = e < TV && t0 + t < L && kv < R;
       pf[n] = in ? *reinterpret_cast<const u32x4*>(D + (t0 + t) * R + kv) : u32x4{0, 0, 0, 0};
     }
@@ -335,8 +351,9 @@ void dt_proj_tile_kernel(const ProjParams p) {
     for (int n = 0; n < NPF; ++n) {
       const int e = tid + n * kThreads;
       if (e < TV) {
-        const int t = e / RV, kv = (e - t * RV) * E;
-        *reinterpret_cast<u32x4*>(&st.d[buf][t][kv]) = pf[n];
+        int t, j;
+        piece(e, t, j);
+        *reinterpret_cast<u32x4*>(&st.d[buf][j][t][0]) = pf[n];
       }
     }
   };
@@ -386,7 +403,7 @@ void dt_proj_tile_kernel(const ProjParams p) {
       // A operands: lane (r16, G) holds delta[t0 + 16 q + r16][kc KC + E G ..]
       u32x4 af[KCH];
 #pragma unroll
-      for (int kc = 0; kc < KCH; ++kc) af[kc] = *reinterpret_cast<const u32x4*>(&st.d[buf][16 * q + r16][kc * KC + E * G]);
+      for (int kc = 0; kc < KCH; ++kc) af[kc] = *reinterpret_cast<const u32x4*>(&st.d[buf][4 * kc + G][16 * q + r16][0]);
       // (the accumulators start from the bias: every register of a lane is
       // one channel, so dt + dt_bias costs no add)
       v4f acc[2] = {{bias[0], bias[0], bias[0], bias[0]}, {bias[1], bias[1], bias[1], bias[1]}};
