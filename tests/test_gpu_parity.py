@@ -86,7 +86,8 @@ def test_workload_full_size_every_element(name, scan_kernel):
 def test_packed_reset_default_kernel_choice(monkeypatch):
     """The library's own choice of tokens per lane (no override): with a reset
     mask and a long sequence on few channels it takes 32 tokens per lane;
-    every element against the oracle."""
+    every element against the oracle. (Its choice of the few-row forms is
+    test_mamba130m_default_kernel_choice.)"""
     for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_SPLIT"):
         monkeypatch.delenv(k, raising=False)
     print("default kernel choice: bf16 1 x 64 x 16 x 8192 with resets", flush=True)
@@ -96,6 +97,22 @@ def test_packed_reset_default_kernel_choice(monkeypatch):
     y, h = run_scan(inp)
     check_close(np64(y), yr, *TOL["bf16"], "y packed_reset default choice")
     check_close(np64(h), hr, *TOL_STATE, "h_last packed_reset default choice")
+
+
+def test_mamba130m_default_kernel_choice(monkeypatch):
+    """The library's own choice of form (no override) at the Mamba-130M layer
+    shape, where it gives each channel row 32 lanes, and at 1 x 3072
+    channels, where it gives 64; every element against the oracle."""
+    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_SPLIT"):
+        monkeypatch.delenv(k, raising=False)
+    print("default kernel choice: mamba130m full size", flush=True)
+    inp, yr, hr = full_size_reference("mamba130m")
+    y, h = run_scan(inp)
+    check_close(np64(y), yr, *TOL["bf16"], "y mamba130m default choice")
+    check_close(np64(h), hr, *TOL_STATE, "h_last mamba130m default choice")
+    print("default kernel choice: bf16 1 x 3072 x 16 x 2048", flush=True)
+    inp = make_case(906, 1, 3072, 16, 2048, "bf16", gate=True, h0=True)
+    compare_full(inp, what="default choice 1x3072x2048")
 
 
 def _edge_mask(kind, batch, L):
