@@ -70,8 +70,8 @@ struct Shape {
 
 // Waves per SIMD the register budget is set for (launch bound). K = 16 with
 // bf16 I/O and no reset mask fits 4 (<= 128 VGPRs); the reset mask and fp32
-// z need more registers and run at 3; K = 32 at 2. The split form in 4-wave
-// blocks runs 3 blocks per CU (LDS), so 3 waves per SIMD.
+// z need more registers and run at 3; K = 32 at 2. Rows of 32 or 64 lanes in
+// 4-wave blocks run 3 blocks per CU (LDS), so 3 waves per SIMD.
 template <typename IoT, int K, bool RESET, int W = 8, int RL = kRowLanes>
 constexpr int min_waves_per_simd() {
   return K == 32 ? 2 : ((RESET || sizeof(IoT) == 4 || (RL > kRowLanes && W == 4)) ? 3 : 4);

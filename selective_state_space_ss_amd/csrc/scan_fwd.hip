@@ -55,13 +55,14 @@ int pick_k(const ScanParams& p) {
 // MI355X, bf16 with gate, seq 2048: 4 x 1536 channels 82.7 -> 61.7 us
 // (32 lanes, 4 waves; 64 lanes: 67.5); 1 x 3072: 80.7 -> 39.8 (64 lanes);
 // 2 x 2048: 81.8 -> 49.1 (32 lanes, 4 waves); 4 x 2048: 85.9 -> 77.9 (32
-// lanes, 8 waves). Only for K = 16 without a reset mask and N <= 16. SS_SCAN_SPLIT=off, =r32w4, =r32w8 or =r64w4 (read at every
-// call) overrides the rule.
+// lanes, 8 waves). Only for K = 16 without a reset mask and N <= 16.
+// SS_SCAN_FORM=plain, =r32w4, =r32w8 or =r64w4 (read at every call)
+// overrides the rule.
 int few_rows_form(const ScanParams& p) {
   if (p.N > 16) return kPlain;
-  if (const char* e = std::getenv("SS_SCAN_SPLIT")) {
+  if (const char* e = std::getenv("SS_SCAN_FORM")) {
     const std::string v(e);
-    if (v == "off") return kPlain;
+    if (v == "plain") return kPlain;
     if (v == "r32w4") return kRows32w4;
     if (v == "r32w8") return kRows32w8;
     if (v == "r64w4") return kRows64w4;

@@ -85,7 +85,7 @@ def to_dev(inp, device="cuda"):
 # and at 32 tokens per lane; its forms for few rows at 16 tokens per lane,
 # rows of 32 lanes (4- and 8-wave blocks) or 64 lanes; and the row-parallel
 # walk. The library picks one by shape; SS_SCAN_KERNEL,
-# SS_SCAN_TOKENS_PER_LANE and SS_SCAN_SPLIT, read at every call, force one.
+# SS_SCAN_TOKENS_PER_LANE and SS_SCAN_FORM, read at every call, force one.
 # (The few-row forms take no reset mask and N <= 16: past that, they run the
 # plain chunked scan.)
 _FORMS = {"rows32": "r32w4", "rows32w8": "r32w8", "rows64": "r64w4"}
@@ -96,4 +96,4 @@ RESET_SCAN_KERNELS = ["chunked", "chunked32", "rows"]
 def force_scan_kernel(monkeypatch, kind):
     monkeypatch.setenv("SS_SCAN_KERNEL", "rows" if kind == "rows" else "chunked")
     monkeypatch.setenv("SS_SCAN_TOKENS_PER_LANE", "32" if kind == "chunked32" else "16")
-    monkeypatch.setenv("SS_SCAN_SPLIT", _FORMS.get(kind, "off"))
+    monkeypatch.setenv("SS_SCAN_FORM", _FORMS.get(kind, "plain"))

@@ -88,7 +88,7 @@ def test_packed_reset_default_kernel_choice(monkeypatch):
     mask and a long sequence on few channels it takes 32 tokens per lane;
     every element against the oracle. (Its choice of the few-row forms is
     test_mamba130m_default_kernel_choice.)"""
-    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_SPLIT"):
+    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_FORM"):
         monkeypatch.delenv(k, raising=False)
     print("default kernel choice: bf16 1 x 64 x 16 x 8192 with resets", flush=True)
     inp = make_case(905, 1, 64, 16, 8192, "bf16", gate=True, h0=True, reset_mean_doc=512)
@@ -103,7 +103,7 @@ def test_mamba130m_default_kernel_choice(monkeypatch):
     """The library's own choice of form (no override) at the Mamba-130M layer
     shape, where it gives each channel row 32 lanes, and at 1 x 3072
     channels, where it gives 64; every element against the oracle."""
-    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_SPLIT"):
+    for k in ("SS_SCAN_TOKENS_PER_LANE", "SS_SCAN_KERNEL", "SS_SCAN_FORM"):
         monkeypatch.delenv(k, raising=False)
     print("default kernel choice: mamba130m full size", flush=True)
     inp, yr, hr = full_size_reference("mamba130m")

@@ -7,7 +7,7 @@ fp64 oracle's per-token states; y and h_last are bitwise those of
 ss_scan_fwd in its plain chunked form (the same kernel with the state
 output switched off; the forms for few rows, which ss_scan_fwd picks at
 these small shapes, combine in another order, so the module forces the plain
-form through SS_SCAN_SPLIT=off).
+form through SS_SCAN_FORM=plain).
 
 The states are fp32 for every I/O type and are held to the fp32 bar."""
 import pytest
@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def plain_scan_form(monkeypatch):
-    monkeypatch.setenv("SS_SCAN_SPLIT", "off")
+    monkeypatch.setenv("SS_SCAN_FORM", "plain")
 
 
 def oracle_states(inp):
