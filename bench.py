@@ -133,7 +133,8 @@ def parse():
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
     ap.add_argument("--counter-workload", metavar="NAME",
                     help="with --counter-pass: run 3 launches of that configuration's scan (tiny_fp32, mamba130m, "
-                         "packed_reset, mamba2p8b) instead of the steps")
+                         "packed_reset, mamba2p8b), or of ss_dt_proj at the producers' shape (dt_proj), instead of "
+                         "the steps")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes into " + TRAFFIC_FILE)
     ap.add_argument("--summarize-trace", metavar="KT_DIR",
@@ -785,7 +786,14 @@ def main():
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
-        if args.counter_workload:
+        if args.counter_workload == "dt_proj":
+            from selective_state_space_ss_amd.workloads import make_producer_case
+            batch, channels, L, W, R = PRODUCER_SHAPE
+            pc = make_producer_case(1030, batch, channels, L, W, R, "bf16", device="cuda")
+            dt = torch.empty(batch, channels, L, dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                ss.ss_dt_proj(pc["w_dt"], pc["delta"], pc["dt_bias"], apply_softplus=True, out=dt)
+        elif args.counter_workload:
             c = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(args.counter_workload).items()}
             for _ in range(3):
                 ss.ss_scan_fwd(c["x"], c["dt"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"], dt_bias=c["dt_bias"],
