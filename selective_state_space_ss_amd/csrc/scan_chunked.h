@@ -310,11 +310,17 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
             load_vec16(Bg + g, vb);
             load_vec16(Cg + g, vc);
           } else {
+            // (offsets recomputed from an opaque copy of s: hoisted out of
+            // the chunk loop for this rare path, they were spilled to scratch)
+            int so = s;
+            asm volatile("" : "+v"(so));
+            const int nlo = so / kSegPerN, no = grp * NG + nlo, tpo = (so - nlo * kSegPerN) * VEC;
+            const int64_t go = (int64_t)no * L + t0 + tpo;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-              const bool in = n < N && t0 + tpos + e < L;
-              vb[e] = in ? Io<IoT>::to_f32(Bg[g + e]) : 0.0f;
-              vc[e] = in ? Io<IoT>::to_f32(Cg[g + e]) : 0.0f;
+              const bool in = no < N && t0 + tpo + e < L;
+              vb[e] = in ? Io<IoT>::to_f32(Bg[go + e]) : 0.0f;
+              vc[e] = in ? Io<IoT>::to_f32(Cg[go + e]) : 0.0f;
             }
           }
 #pragma unroll
@@ -477,8 +483,19 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
     }
   }
 
-  if (p.h_last && row_ok)
-    for (int n = tl; n < N; n += RL) p.h_last[(b * p.channels + c) * N + n] = sCarry[slot + n];
+  // The row's place is recomputed here from an opaque copy of the thread
+  // index: kept live from the prologue across the chunk loop, these values
+  // were spilled to scratch.
+  if (p.h_last) {
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    const int wave_e = tid_e >> 6, lane_e = tid_e & 63, row_e = lane_e / RL, tl_e = lane_e % RL;
+    const int64_t ce = (blk - b * p.chan_blocks) * S::kChan + wave_e * RPW + row_e;
+    if (ce < p.channels) {
+      const int slot_e = (wave_e * RPW + row_e) * NMAX;
+      for (int n = tl_e; n < N; n += RL) p.h_last[(b * p.channels + ce) * N + n] = sCarry[slot_e + n];
+    }
+  }
 }
 
 template <typename IoT, int K, int W, int NMAX, bool GATE, bool RESET, int STATES, int CW = 0, int RL = kRowLanes>
