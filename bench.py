@@ -566,7 +566,20 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
                                "io": wd.io_dtype, "gate": wd.gate},
                      "warm": decode_roofline(wd, time_launches(fd, stream, reps)),
                      "cold": decode_roofline(wd, time_cold(fd, stream, reps, flush))}
-    del flush, state
+    # The achievable rate of the decode's access pattern on this machine: an
+    # in-place read-modify-write of a tensor of the state's size (torch's own
+    # elementwise kernel), timed the same two ways.
+    buf = torch.randn_like(state)
+    fc = lambda: buf.mul_(1.0000001)
+    moved = 2 * buf.numel() * buf.element_size()
+    ceil = {"bytes_moved": moved}
+    for kind, us in (("warm", time_launches(fc, stream, reps)), ("cold", time_cold(fc, stream, reps, flush))):
+        gbs = moved / (us * 1e-6) / 1e9
+        ceil[kind] = {"us": round(us, 2), "GB_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        dec = res["decode"][kind]
+        dec["frac_of_inplace_rw"] = round(dec["GB_s"] / gbs, 4)
+    res["decode"]["inplace_rw_same_size"] = ceil
+    del flush, state, buf
     return res
 
 
