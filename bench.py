@@ -477,8 +477,9 @@ def measure_fused_conv(ss, P, w, stream, rates, reps: int = 20):
 def measure_producers(ss, stream, reps: int = 20):
     """The scan's input side at the Mamba-2.8B layer shape (batch 8, channels
     5120, seq 2048, bf16): ss_conv1d_silu (width 4; bytes: read x_pre, write
-    x) and ss_dt_proj (rank 160, with bias and softplus; bytes: read w_dt and
-    delta, write dt; flops 2 R per output). Per-launch HIP-event averages."""
+    x) and ss_dt_proj (rank 160, with bias and softplus, and without them;
+    bytes: read w_dt and delta, write dt; flops 2 R per output). Per-launch
+    HIP-event averages."""
     import torch
     from selective_state_space_ss_amd.workloads import make_producer_case
     batch, channels, L, W, R = PRODUCER_SHAPE
@@ -491,6 +492,11 @@ def measure_producers(ss, stream, reps: int = 20):
         "ss_dt_proj": (lambda: ss.ss_dt_proj(c["w_dt"], c["delta"], c["dt_bias"], apply_softplus=True, out=dt),
                        batch * channels * L * 2 + batch * L * R * 2 + channels * R * 2 + channels * 4,
                        2.0 * batch * channels * L * R),
+        # the plain product, as a Mamba layer feeds its scan (which then
+        # applies softplus(dt + dt_bias) itself)
+        "ss_dt_proj_raw": (lambda: ss.ss_dt_proj(c["w_dt"], c["delta"], None, apply_softplus=False, out=dt),
+                           batch * channels * L * 2 + batch * L * R * 2 + channels * R * 2,
+                           2.0 * batch * channels * L * R),
     }
     res = {"shape": {"batch": batch, "channels": channels, "seq": L, "width": W, "rank": R, "io": "bf16"}}
     for name, (f, nbytes, flops) in calls.items():
