@@ -24,6 +24,11 @@ PROBE_LIB = os.path.join(PKG, "libssprobe.so")
 PROBE_SOURCES = ["probe_issue.hip", "probe_lds.hip"]
 ARCH = "gfx950"
 
+# the race check of the chunked scan's B/C stage (tests only): the sources
+# that instantiate the chunked kernel, rebuilt with SS_LDS_POISON=1 and linked
+# with the other objects of the library
+POISON_LIB = os.path.join(PKG, "libssscan_lds_poison.so")
+POISON_SOURCES = ["scan_fwd.hip", "scan_fwd_reset.hip", "scan_fwd_conv.hip", "scan_states.hip"]
 SOURCES = ["ss_abi.hip", "scan_fwd.hip", "scan_fwd_reset.hip", "scan_fwd_conv.hip", "scan_states.hip", "scan_rows.hip", "state_update.hip", "gated_scan.hip", "effective_attention.hip", "producers.hip"]
 
 HIPCC_FLAGS = [
@@ -69,19 +74,23 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     objs = []
 
-    def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        out = _run([cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        src, poison = job
+        obj = os.path.join(BUILD, src.replace(".hip", "_lds_poison.o" if poison else ".o"))
+        defs = ["-DSS_LDS_POISON=1"] if poison else []
+        out = _run([cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *defs, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out:
             print(out)
         return obj
 
-    srcs = SOURCES + PROBE_SOURCES
-    with ThreadPoolExecutor(len(srcs)) as ex:
-        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
-    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+    jobs = [(s, False) for s in SOURCES + PROBE_SOURCES] + [(s, True) for s in POISON_SOURCES]
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        objs = dict(zip(jobs, ex.map(compile_one, jobs)))
+    poison_objs = [objs[(n, n in POISON_SOURCES)] for n in SOURCES]
+    for lib, names in ((LIB, [objs[(n, False)] for n in SOURCES]), (PROBE_LIB, [objs[(n, False)] for n in PROBE_SOURCES]),
+                       (POISON_LIB, poison_objs)):
         tmp = lib + ".tmp%d" % os.getpid()
-        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[objs[n] for n in names]])
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *names])
         os.replace(tmp, lib)
     return LIB
 

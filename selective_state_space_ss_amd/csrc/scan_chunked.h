@@ -43,6 +43,16 @@
 
 #include <cmath>
 
+// SS_LDS_POISON=1 builds the race check of the B/C stage (a debug library,
+// libssscan_lds_poison.so): before every fill the whole stage is set to NaN
+// between two barriers, so an operand read that the fill's barrier did not
+// order after the fill returns NaN, and a write racing a previous reader
+// poisons that reader's result. The outputs of a correct kernel are bitwise
+// those of the normal build.
+#ifndef SS_LDS_POISON
+#define SS_LDS_POISON 0
+#endif
+
 namespace ss {
 namespace {
 
@@ -294,6 +304,15 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
     // check.
     auto stage = [&](int grp) {
       __syncthreads();
+      if constexpr (SS_LDS_POISON != 0) {
+        float* sb = &sB[0][0][0];
+        float* sc = &sC[0][0][0];
+        for (int i = tid; i < NG * RL * KP; i += S::kThreads) {
+          sb[i] = __builtin_nanf("");
+          sc[i] = __builtin_nanf("");
+        }
+        __syncthreads();
+      }
       {
         constexpr int kSegPerN = T / VEC;
         constexpr int kSeg = NG * kSegPerN;
