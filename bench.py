@@ -510,6 +510,7 @@ def measure_producers(ss, stream, reps: int = 20):
 
 
 FLUSH_BYTES = 1 << 30
+PCT_REPS = 50   # launches behind each configuration's p10 / median / p90
 
 
 def time_cold(f, stream, reps: int, flush) -> float:
@@ -531,7 +532,33 @@ def time_cold(f, stream, reps: int, flush) -> float:
         f()
         e1.record(stream)
     torch.cuda.synchronize()
-    return sum(e0.elapsed_time(e1) for e0, e1 in pairs) / reps * 1e3
+    each = [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+    LAST_EACH[:] = each
+    return sum(each) / reps
+
+
+# per-launch microseconds of the last time_cold / time_each call
+LAST_EACH: list = []
+
+
+def time_each(f, stream, reps: int) -> list:
+    """Microseconds of each of `reps` back-to-back launches of f (an event pair
+    around every launch; the caches keep what the previous launch left)."""
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in pairs:
+        e0.record(stream)
+        f()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+
+
+def percentiles(each: list) -> dict:
+    """p10 / median / p90 of per-launch times (nearest rank)."""
+    v = sorted(each)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"p10_us": round(pick(0.1), 2), "median_us": round(pick(0.5), 2), "p90_us": round(pick(0.9), 2)}
 
 
 def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
@@ -541,7 +568,8 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
     Mamba-2.8B layer (the step's scan) and the decode step. Each is timed
     back to back after a warm-up (warm: the inputs of a small case stay in
     the 256 MB last-level cache between launches) and with the caches flushed
-    before every launch (cold)."""
+    before every launch (cold). Each also carries p10 / median / p90 of 50
+    launches timed one by one (an event pair around every launch)."""
     import torch
     from selective_state_space_ss_amd.workloads import WORKLOADS, make_inputs
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -558,7 +586,9 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
                                                  dt_bias=d["dt_bias"], h0=d["h0"], reset=d["reset"], y=y,
                                                  h_last=h)
         warm = scan_roofline(w, time_launches(f, stream, reps), rates)
-        cold = scan_roofline(w, time_cold(f, stream, reps, flush), rates)
+        warm.update(percentiles(time_each(f, stream, PCT_REPS)))
+        cold = scan_roofline(w, time_cold(f, stream, PCT_REPS, flush), rates)
+        cold.update(percentiles(LAST_EACH))
         res[name] = {"shape": {"batch": w.batch, "channels": w.channels, "state_dim": w.state_dim,
                                "seq": w.seqlen, "io": w.io_dtype, "gate": w.gate, "h0": w.h0 is not None,
                                "reset": w.reset_mean_doc is not None},
@@ -571,7 +601,9 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
     res["decode"] = {"shape": {"batch": wd.batch, "channels": wd.channels, "state_dim": wd.state_dim,
                                "io": wd.io_dtype, "gate": wd.gate},
                      "warm": decode_roofline(wd, time_launches(fd, stream, reps)),
-                     "cold": decode_roofline(wd, time_cold(fd, stream, reps, flush))}
+                     "cold": decode_roofline(wd, time_cold(fd, stream, PCT_REPS, flush))}
+    res["decode"]["cold"].update(percentiles(LAST_EACH))
+    res["decode"]["warm"].update(percentiles(time_each(fd, stream, PCT_REPS)))
     # The achievable rate of the decode's access pattern on this machine: an
     # in-place read-modify-write of a tensor of the state's size (torch's own
     # elementwise kernel), timed the same two ways.

@@ -131,3 +131,10 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_percentiles_nearest_rank():
+    each = [float(v) for v in range(1, 51)]          # 1 .. 50 us, shuffled order must not matter
+    p = bench.percentiles(each[::-1])
+    assert p == {"p10_us": 6.0, "median_us": 25.0, "p90_us": 45.0}
+    assert bench.percentiles([7.0]) == {"p10_us": 7.0, "median_us": 7.0, "p90_us": 7.0}
