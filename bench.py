@@ -643,6 +643,44 @@ def probe_live():
 COPY_CEILING_BYTES = 1 << 30   # each way
 
 
+def measure_two_streams(ss, P, Dd, y, h_last, yd, state, stream, steps: int = 50):
+    """The bench step with its two independent halves on two streams: the
+    prompt scan (VALU-bound) on the bench stream and the decode update
+    (HBM-bound, its own batch) on a second stream of default priority, so the
+    decode's memory traffic can run under the scan's arithmetic. Steps stay
+    ordered per stream (the decode's state is updated in place). Reports the
+    time per step next to the sequential step's figure."""
+    import torch
+    side = torch.cuda.Stream()
+
+    def scan():
+        ss.ss_scan_fwd(P["x"], P["dt"], P["A"], P["B"], P["C"], D=P["D"], z=P["z"], dt_bias=P["dt_bias"],
+                       h0=P["h0"], y=y, h_last=h_last, stream=stream)
+
+    def decode():
+        ss.ss_state_update(state, Dd["x"], Dd["dt"], Dd["A"], Dd["B"], Dd["C"], D=Dd["D"], z=Dd["z"],
+                           dt_bias=Dd["dt_bias"], y=yd, stream=side)
+
+    def run(n):
+        side.wait_stream(stream)
+        for _ in range(n):
+            scan()
+            decode()
+        stream.wait_stream(side)
+
+    t0 = time.time()
+    while time.time() - t0 < EXTRA_WARM_S:
+        run(5)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"steps": steps, "us_per_step": round(e0.elapsed_time(e1) / steps * 1e3, 2)}
+
+
 def measure_copy(stream, reps: int = 20):
     """A plain device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB), the
     achievable streaming rate on this machine next to the 8 TB/s peak."""
@@ -935,6 +973,10 @@ def main():
                          "producers": measure_producers(ss, stream),
                          "ss_scan_fwd_conv": measure_fused_conv(ss, P, wp, stream, rates),
                          "stream_copy_1GiB": measure_copy(stream)}
+        two = measure_two_streams(ss, P, Dd, y, h_last, yd, state, stream)
+        two["GB_s"] = round((bytes_p + bytes_d) / (two["us_per_step"] * 1e-6) / 1e9, 1)
+        two["sequential_us_per_step"] = round(ms_step * 1e3, 2)
+        out["extras"]["step_two_streams"] = two
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
