@@ -188,8 +188,15 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
   __shared__ float sB[NG][RL][KP];
   __shared__ float sC[NG][RL][KP];
   __shared__ float sA2[S::kChan * NMAX];     // A[c, n] * log2(e) per row of the block
-  __shared__ float sCarry[S::kChan * NMAX];  // state entering the current chunk
-  __shared__ float sZero[NMAX];              // what lanes 1..15 read in place of the carry
+  // sCarry: the state entering the current chunk, per row; then, 8 dwords
+  // on, sZero: what the other lanes of a row read in place of the carry.
+  // With N_max >= 16 every row's carry sits a multiple of 16 dwords from the
+  // first, so a zero row 8 dwords off that grid never shares a bank with
+  // the carries that lane 0 of each row reads in the same instruction.
+  __shared__ float sCarryZero[S::kChan * NMAX + 8 + NMAX];
+  float* const sCarry = sCarryZero;
+  float* const sZero = sCarryZero + S::kChan * NMAX + 8;
+  static_assert((S::kChan * NMAX) % 16 == 0, "row carries on a 16-dword grid");
   // kAllStates: one coordinate's states of the chunk per row, each lane's K
   // tokens padded to KP, re-read in token order for coalesced stores
   __shared__ __align__(16) float sSt[STATES == kAllStates ? S::kChan : 1][STATES == kAllStates ? kRowLanes * KP : 1];
@@ -316,11 +323,26 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
       {
         constexpr int kSegPerN = T / VEC;
         constexpr int kSeg = NG * kSegPerN;
+        // Segment u of a coordinate's chunk (VEC tokens, one 16-byte load)
+        // goes to lane row sl at token sj: the 8 threads of a group of 8
+        // take the same piece of 8 consecutive lane rows. Their LDS rows
+        // are KP / 4 (odd) 16-byte slots apart, so the group's 16-byte
+        // stores fall in 8 different groups of 4 banks (the LDS serves such
+        // stores 8 lanes at a time over 32 banks). A wave's load still
+        // covers whole coordinate rows of the chunk.
+        static_assert((KP / 4) % 2 == 1 && RL % 8 == 0 && kSegPerN % 8 == 0, "conflict-free staging order");
+        auto place = [](int u, int& sl, int& sj) {
+          constexpr int kRowGroups = RL / 8;
+          const int gg = u >> 3;
+          sl = 8 * (gg % kRowGroups) + (u & 7);
+          sj = (gg / kRowGroups) * VEC;
+        };
         for (int s = tid; s < kSeg; s += S::kThreads) {
           const int nl = s / kSegPerN;
           const int n = grp * NG + nl;
-          const int tpos = (s - nl * kSegPerN) * VEC;
-          const int sl = tpos / K, sj = tpos - sl * K;
+          int sl, sj;
+          place(s - nl * kSegPerN, sl, sj);
+          const int tpos = sl * K + sj;
           float vb[VEC], vc[VEC];
           const int64_t g = (int64_t)n * L + t0 + tpos;
           // (each branch stores its own values: with one shared set the
@@ -333,7 +355,10 @@ __global__ __launch_bounds__(64 * W, (min_waves_per_simd<IoT, K, RESET, W, RL>()
             // the chunk loop for this rare path, they were spilled to scratch)
             int so = s;
             asm volatile("" : "+v"(so));
-            const int nlo = so / kSegPerN, no = grp * NG + nlo, tpo = (so - nlo * kSegPerN) * VEC;
+            const int nlo = so / kSegPerN, no = grp * NG + nlo;
+            int slo, sjo;
+            place(so - nlo * kSegPerN, slo, sjo);
+            const int tpo = slo * K + sjo;
             const int64_t go = (int64_t)no * L + t0 + tpo;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
