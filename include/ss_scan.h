@@ -26,7 +26,8 @@
  *  - io_dtype (ss_dtype) is the element type of x, dt, z, B, C and y.
  *    A, D, dt_bias, h0, h_last and state are always float32.
  *  - The call enqueues its kernel on `stream` (a hipStream_t; NULL = the
- *    default stream) and returns without synchronising.
+ *    default stream) and returns without synchronising, so it can be
+ *    recorded by stream capture into a HIP graph and replayed.
  *  - Arguments are validated before anything is enqueued; a validation
  *    error returns its ss_status with no side effect. A failed launch returns
  *    SS_ERR_HIP.
