@@ -133,8 +133,8 @@ def parse():
                     help="run a 256 MiB device copy, then 3 steps, for a rocprofv3 --pmc pass (no JSON)")
     ap.add_argument("--counter-workload", metavar="NAME",
                     help="with --counter-pass: run 3 launches of that configuration's scan (tiny_fp32, mamba130m, "
-                         "packed_reset, mamba2p8b), or of ss_dt_proj at the producers' shape (dt_proj), instead of "
-                         "the steps")
+                         "packed_reset, mamba2p8b), of ss_dt_proj at the producers' shape (dt_proj) or of "
+                         "ss_gated_scan at its bench shape (gated), instead of the steps")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes into " + TRAFFIC_FILE)
     ap.add_argument("--summarize-trace", metavar="KT_DIR",
@@ -882,6 +882,14 @@ def main():
             dt = torch.empty(batch, channels, L, dtype=torch.bfloat16, device=dev)
             for _ in range(3):
                 ss.ss_dt_proj(pc["w_dt"], pc["delta"], pc["dt_bias"], apply_softplus=True, out=dt)
+        elif args.counter_workload == "gated":
+            from selective_state_space_ss_amd.workloads import make_gated_case
+            batch, L, dk, dv = GATED_SHAPE
+            gc = make_gated_case(1010, batch, L, dk, dv, "bf16", device="cuda")
+            gy = torch.empty(batch, L, dv, dtype=torch.bfloat16, device=dev)
+            gs = torch.empty(batch, dk, dv, dtype=torch.float32, device=dev)
+            for _ in range(3):
+                ss.ss_gated_scan(gc["q"], gc["k"], gc["v"], gc["gamma"], y=gy, final_state=gs)
         elif args.counter_workload:
             c = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(args.counter_workload).items()}
             for _ in range(3):

@@ -170,16 +170,20 @@ struct Stage;
 // same element order, which is all the product needs.
 template <typename St, int RT>
 __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int G, int c16) {
+  // the lane's swizzled offsets within its rows of q and k (St::sw): the
+  // pieces' bit is below the multiples of 16 and 32 added to them
+  const int o8 = St::sw(c16, 8 * G), o4 = St::sw(c16, 4 * G);
+  const int oc = St::sw(4 * G + (c16 >> 2), 4 * (c16 & 3));
   // A^T[s][t] = k_s . q_t over dk: 32 indices per MFMA, 16 for an odd tile
   v4f At = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int ch = 0; ch < RT / 2; ++ch) {
-    const u32x4 ka = *reinterpret_cast<const u32x4*>(&s.k[c16][32 * ch + 8 * G]);
-    const u32x4 qa = *reinterpret_cast<const u32x4*>(&s.q[c16][32 * ch + 8 * G]);
+    const u32x4 ka = *reinterpret_cast<const u32x4*>(&s.k[c16][32 * ch + o8]);
+    const u32x4 qa = *reinterpret_cast<const u32x4*>(&s.q[c16][32 * ch + o8]);
     At = mfma32(ka, qa, At);
   }
   if constexpr (RT % 2 == 1) {
-    const int i = 16 * (RT - 1) + 4 * G;
+    const int i = 16 * (RT - 1) + o4;
     At = mfma16(ld2w(&s.k[c16][i]), ld2w(&s.q[c16][i]), At);
   }
   // Y = (A o L) V: M[t][4 G + r] in register r is the A operand of token
@@ -197,14 +201,14 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
   v4f Z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int pr = 0; pr < RT / 2; ++pr) {
-    const u32x4 qa = cat(ld2w(&s.q[c16][32 * pr + 4 * G]), ld2w(&s.q[c16][32 * pr + 16 + 4 * G]));
+    const u32x4 qa = cat(ld2w(&s.q[c16][32 * pr + o4]), ld2w(&s.q[c16][32 * pr + 16 + o4]));
     const Split4 s0 = split4(S[2 * pr]), s1 = split4(S[2 * pr + 1]);
     Z = mfma32(qa, cat(s0.hi, s1.hi), Z);
     Z = mfma32(qa, cat(s0.mid, s1.mid), Z);
     Z = mfma32(qa, cat(s0.lo, s1.lo), Z);
   }
   if constexpr (RT % 2 == 1) {
-    const u32x2 qa = ld2w(&s.q[c16][16 * (RT - 1) + 4 * G]);
+    const u32x2 qa = ld2w(&s.q[c16][16 * (RT - 1) + o4]);
     const Split4 sl = split4(S[RT - 1]);
     Z = mfma16(qa, sl.hi, Z);
     Z = mfma16(qa, sl.mid, Z);
@@ -221,7 +225,7 @@ __device__ __forceinline__ v4f chunk_bf16(const St& s, v4f (&S)[RT], int w, int 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     // k of tokens 4 G .. 4 G + 3 for row 16 rt + c16 (the A operand)
-    const u32x2 kt = ld_col4(&s.k[4 * G + (c16 >> 2)][16 * rt + 4 * (c16 & 3)]);
+    const u32x2 kt = ld_col4(&s.k[4 * G + (c16 >> 2)][16 * rt + oc]);
     S[rt] *= p15;
     S[rt] = mfma16(kt, ws.hi, S[rt]);
     S[rt] = mfma16(kt, ws.mid, S[rt]);
@@ -238,6 +242,16 @@ struct Stage {
   static constexpr int VGS = 4 * kCols + 64;              // group stride of the grouped v
   static constexpr bool kGrouped = sizeof(E) == 4;      // fp32: token-grouped copies of k and v
   static constexpr int VS = kCols + 16 / (int)sizeof(E);  // row stride of the row-major v (bf16)
+  // Element e of row t of q or k sits at sw(t, e): rows 8..15 swap the
+  // 16-byte pieces of each pair. A row of q or k is twice an odd number of
+  // 16-byte slots long (mod the 16 slots that span the 64 banks; for bf16
+  // when dk is a multiple of 32), so rows 0..7 of one piece land in 8
+  // different even slot groups, and with the swap rows 8..15 in the 8 odd
+  // ones: the 16 lanes of a quarter wave reading one piece of 16 rows hit 16
+  // different groups of 4 banks (without the swap, rows r and r + 8 share).
+  static constexpr int PE = 16 / (int)sizeof(E);  // elements per 16-byte piece
+  static __device__ __forceinline__ int sw(int t, int e) { return e ^ (((t >> 3) & 1) * PE); }
+  static_assert(DKP % (2 * PE) == 0, "pieces swapped in pairs");
   E q[kT][QS];
   E k[kT][QS];
   E kg[kGrouped ? 4 * KGS : 1];  // fp32: k[t][i] at [t / 4][i][t % 4]
@@ -349,8 +363,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
         if (e < QV) {
           const int t = e / (DKP / VEC_E);
           const int i = (e - t * (DKP / VEC_E)) * VEC_E;
-          *reinterpret_cast<u32x4*>(&s.q[t][i]) = qr[n];
-          *reinterpret_cast<u32x4*>(&s.k[t][i]) = kr[n];
+          *reinterpret_cast<u32x4*>(&s.q[t][St::sw(t, i)]) = qr[n];
+          *reinterpret_cast<u32x4*>(&s.k[t][St::sw(t, i)]) = kr[n];
           if constexpr (St::kGrouped) {
 #pragma unroll
             for (int x = 0; x < VEC_E; ++x) s.kg[(t >> 2) * St::KGS + (i + x) * 4 + (t & 3)] = elem<IoT>(kr[n], x);
@@ -373,8 +387,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
         const bool in = t0 + t < L && i < dk;
         const IoT qv = in ? qg[(t0 + t) * dk + i] : zero_elem<IoT>();
         const IoT kv = in ? kgp[(t0 + t) * dk + i] : zero_elem<IoT>();
-        s.q[t][i] = qv;
-        s.k[t][i] = kv;
+        s.q[t][St::sw(t, i)] = qv;
+        s.k[t][St::sw(t, i)] = kv;
         if constexpr (St::kGrouped) s.kg[(t >> 2) * St::KGS + i * 4 + (t & 3)] = kv;
       }
       for (int e = tid; e < kT * kCols; e += kThreads) {
@@ -419,11 +433,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
     } else {
       // A^T[s][t] = k_s . q_t: register r at lane (t, G) is s = 4 G + r
       v4f A0 = {0.0f, 0.0f, 0.0f, 0.0f}, A1 = A0;
+      const int o4 = St::sw(c16, 4 * G);  // the lane's swizzled offset in its rows of q and k
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int i = 16 * rt + 4 * G;
-        const v4f ka = ld4(&s.k[c16][i]);
-        const v4f qa = ld4(&s.q[c16][i]);
+        const v4f ka = ld4(&s.k[c16][16 * rt + o4]);
+        const v4f qa = ld4(&s.q[c16][16 * rt + o4]);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (rt & 1) A1 = mfma4(ka[g], qa[g], A1);
@@ -441,7 +455,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT <= 
       v4f Z0 = {0.0f, 0.0f, 0.0f, 0.0f}, Z1 = Z0;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const v4f qa = ld4(&s.q[c16][16 * rt + 4 * G]);  // read again: fewer live registers
+        const v4f qa = ld4(&s.q[c16][16 * rt + o4]);  // read again: fewer live registers
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           if (rt & 1) Z1 = mfma4(qa[g], S[rt][g], Z1);
