@@ -298,6 +298,35 @@ def summarize_trace(kt_dir):
             name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
         print(f"| `{short}` | {grid} | {block} | {len(d)} | {sum(d) / len(d):.0f} | {statistics.median(d):.0f} | "
               f"{min(d)} | {max(d)} | {100.0 * sum(d) / total:.2f} % |")
+    step = step_launches(files)
+    if step:
+        d = sorted(step)
+        print()
+        print(f"In the bench step: {len(d)} decode launches that start after a Mamba-2.8B prompt scan ends (the "
+              f"step's order; the two-stream extra's overlapping ones excluded): mean {sum(d) / len(d):.0f} ns, "
+              f"median {statistics.median(d):.0f} ns, p10 {d[len(d) // 10]} ns, p90 {d[9 * len(d) // 10]} ns.")
+
+
+STEP_SCAN = "scan_fwd_kernel<ss::bf16_t, 16, 8, 16, true, false, 0, 0, 16>"
+STEP_DECODE = "state_update_kernel<ss::bf16_t, 1, true, true>"
+
+
+def step_launches(files) -> list:
+    """Durations (ns) of the decode launches that directly follow a launch of
+    the Mamba-2.8B prompt scan in start order and begin after it has ended:
+    the decode of the bench step, cold after the scan, as the kernel itself
+    ran (no HIP events around it)."""
+    import csv
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    out = []
+    for (s0, e0, n0), (s1, e1, n1) in zip(rows, rows[1:]):
+        if STEP_SCAN in n0 and STEP_DECODE in n1 and s1 >= e0:
+            out.append(e1 - s1)
+    return out
 
 
 def recorded_traffic():

@@ -138,3 +138,26 @@ def test_percentiles_nearest_rank():
     p = bench.percentiles(each[::-1])
     assert p == {"p10_us": 6.0, "median_us": 25.0, "p90_us": 45.0}
     assert bench.percentiles([7.0]) == {"p10_us": 7.0, "median_us": 7.0, "p90_us": 7.0}
+
+
+def test_step_decode_launches_follow_the_scan(tmp_path, capsys):
+    path = tmp_path / "kt" / "kt_kernel_trace.csv"
+    os.makedirs(path.parent)
+    names = ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Workgroup_Size_X", "Workgroup_Size_Y",
+             "Workgroup_Size_Z", "Start_Timestamp", "End_Timestamp"]
+    scan = "void ss::(anonymous namespace)::scan_fwd_kernel<ss::bf16_t, 16, 8, 16, true, false, 0, 0, 16>(ss::ScanParams)"
+    dec = "void ss::(anonymous namespace)::state_update_kernel<ss::bf16_t, 1, true, true>(ss::UpdateParams)"
+    rows = [(scan, 0, 300), (dec, 302, 330),          # a step: counted (28)
+            (scan, 400, 700), (dec, 705, 735),        # a step: counted (30)
+            (dec, 740, 770),                          # a warm launch after a decode: not counted
+            (scan, 800, 1100), (dec, 900, 1000),      # overlapping the scan (two streams): not counted
+            ]
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(names)
+        for name, s, e in rows:
+            wr.writerow([name, 1, 1, 1, 256, 1, 1, s, e])
+    assert sorted(bench.step_launches([str(path)])) == [28, 30]
+    bench.summarize_trace(str(tmp_path / "kt"))
+    out = capsys.readouterr().out
+    assert "In the bench step: 2 decode launches" in out and "mean 29 ns" in out
