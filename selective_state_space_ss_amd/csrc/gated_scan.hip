@@ -62,13 +62,8 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Four consecutive staged elements, widened to fp32.
+// Four consecutive staged fp32 elements (the fp32 path).
 __device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
-__device__ __forceinline__ v4f ld4(const bf16_t* p) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  return v4f{__builtin_bit_cast(float, w.x << 16), __builtin_bit_cast(float, w.x & 0xffff0000u),
-             __builtin_bit_cast(float, w.y << 16), __builtin_bit_cast(float, w.y & 0xffff0000u)};
-}
 
 template <typename E>
 __device__ __forceinline__ E zero_elem() {
