@@ -147,6 +147,12 @@ def parse():
                          "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS pass), print the pattern names as JSON, exit")
     ap.add_argument("--summarize-lds", metavar="PMC_DIR",
                     help="print a markdown table of conflict cycles per instruction from a --probe-lds pass, exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="print a markdown table of the counters of --pmc passes (one directory per pass) over the "
+                         "dispatches of the kernel named by --counter-kernel: each counter summed over the chip's "
+                         "counter instances per dispatch, then the median over the dispatches; exit")
+    ap.add_argument("--counter-kernel", metavar="SUBSTRING", default="scan_fwd_kernel",
+                    help="with --summarize-counters: the kernel name to select (a substring)")
     return ap.parse_args()
 
 
@@ -844,8 +850,40 @@ def summarize_lds(pmc_dir: str):
         print(f"| {name} | {width} | {c.get('SQ_LDS_BANK_CONFLICT', 0.0) / LDS_PROBE_ITERS:.2f} |")
 
 
+def summarize_counters(pmc_dirs, kernel: str):
+    """Counter table of one kernel over rocprofv3 --pmc passes: per dispatch
+    and counter, the sum over the counter's instances (XCDs, SEs, ...); then,
+    per counter, the median over the selected dispatches."""
+    import csv
+    import glob
+    import statistics
+    per = {}  # counter -> {(pass, dispatch): value}
+    names = set()
+    for d in pmc_dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                names.add(r["Kernel_Name"])
+                key = (f, int(r["Dispatch_Id"]))
+                c = per.setdefault(r["Counter_Name"], {})
+                c[key] = c.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel!r} in {pmc_dirs}")
+    print("Kernel(s): " + "; ".join(f"`{n}`" for n in sorted(names)))
+    print()
+    print("| counter | value | dispatches |")
+    print("|---|---|---|")
+    for name in sorted(per):
+        v = list(per[name].values())
+        print(f"| {name} | {statistics.median(v):,.0f} | {len(v)} |")
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.counter_kernel)
+        return
     if args.summarize_lds:
         summarize_lds(args.summarize_lds)
         return

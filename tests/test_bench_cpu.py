@@ -161,3 +161,25 @@ def test_step_decode_launches_follow_the_scan(tmp_path, capsys):
     bench.summarize_trace(str(tmp_path / "kt"))
     out = capsys.readouterr().out
     assert "In the bench step: 2 decode launches" in out and "mean 29 ns" in out
+
+
+def test_summarize_counters_sums_instances_then_takes_the_median(tmp_path, capsys):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    # three dispatches of the scan, two counter instances each; one copy dispatch that must be ignored
+    for d, vals in ((1, (10.0, 1.0)), (2, (20.0, 2.0)), (3, (40.0, 4.0))):
+        for v in vals:
+            rows.append({"Dispatch_Id": d, "Kernel_Name": "void ss::scan_fwd_kernel<x>(p)",
+                         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": v})
+    rows.append({"Dispatch_Id": 4, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "SQ_INSTS_VALU",
+                 "Counter_Value": 1e9})
+    os.makedirs(tmp_path / "p1")
+    with open(tmp_path / "p1" / "p1_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        w.writerows(rows)
+    bench.summarize_counters([str(tmp_path / "p1")], "scan_fwd_kernel")
+    out = capsys.readouterr().out
+    # per dispatch 11, 22, 44 -> median 22
+    assert "| SQ_INSTS_VALU | 22 | 3 |" in out
+    assert "copyBuffer" not in out
