@@ -766,7 +766,56 @@ def cpu_baseline(inp, w, budget_s: float):
         "sample": f"{done_rows} of {w.batch * w.channels} (batch, channel) rows of the {w.name} prompt scan "
                   f"({ct} channel-tokens, fp64 sequential token loop, {t_total:.1f} s wall)",
         "channel_tokens_per_s": round(ct / t_total, 1),
+        "wall_s": round(t_total, 3),
+        "host": host_cpu(),
     }
+
+
+def host_cpu():
+    """The host's CPU model and counts (the oracle's threads are capped at a
+    one-GPU share of them)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_single_thread(names=("tiny_fp32", "mamba130m"), budget_s: float = 1.5):
+    """The oracle on one thread over whole (b, c) rows of small prompt
+    workloads (the tiny case whole; others until the budget is spent)."""
+    import oracle
+    from selective_state_space_ss_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        rows = max(1, min(w.channels, 8))  # channels per call
+        inp = make_inputs(w, batch=1)
+        t_total, done = 0.0, 0
+        c0 = 0
+        while done < w.channels and (t_total < budget_s or done == 0):
+            cs = slice(c0, min(c0 + rows, w.channels))
+            f64 = lambda t: t[:, cs].double().numpy()
+            kw = dict(D=inp["D"][cs].double().numpy(), z=f64(inp["z"]) if inp["z"] is not None else None,
+                      dt_bias=inp["dt_bias"][cs].double().numpy(),
+                      h0=f64(inp["h0"]) if inp["h0"] is not None else None, threads=1)
+            t0 = time.perf_counter()
+            oracle.scan(f64(inp["x"]), f64(inp["dt"]), inp["A"][cs].double().numpy(), inp["B"].double().numpy(),
+                        inp["C"].double().numpy(), **kw)
+            t_total += time.perf_counter() - t0
+            done += cs.stop - cs.start
+            c0 = cs.stop
+        ct = done * w.seqlen
+        bytes_per_ct = algorithmic_bytes(w) / (w.batch * w.channels * w.seqlen)
+        out[name] = {"rows": done, "channel_tokens": ct, "wall_s": round(t_total, 4),
+                     "channel_tokens_per_s": round(ct / t_total, 1),
+                     "GB_s": round(ct * bytes_per_ct / t_total / 1e9, 5)}
+    return out
 
 
 # LDS bank probe (libssprobe.so ssprobe_lds): (name, access bytes, write?,
@@ -1053,7 +1102,11 @@ def main():
         two["sequential_us_per_step"] = round(ms_step * 1e3, 2)
         out["extras"]["step_two_streams"] = two
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cpu_p, wp, args.cpu_seconds)
+        cb = cpu_baseline(cpu_p, wp, args.cpu_seconds)
+        # the GPU's speed-up over the oracle on the same workload and unit (the scan's kernel time)
+        cb["gpu_speedup"] = round(out["kernels"]["ss_scan_fwd"]["GB_s"] / cb["value"], 1)
+        cb["single_thread"] = cpu_single_thread()
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -183,3 +183,12 @@ def test_summarize_counters_sums_instances_then_takes_the_median(tmp_path, capsy
     # per dispatch 11, 22, 44 -> median 22
     assert "| SQ_INSTS_VALU | 22 | 3 |" in out
     assert "copyBuffer" not in out
+
+
+def test_single_thread_oracle_timing_and_host_info():
+    r = bench.cpu_single_thread(names=("tiny_fp32",), budget_s=0.1)["tiny_fp32"]
+    w = WORKLOADS["tiny_fp32"]
+    assert r["rows"] == w.channels and r["channel_tokens"] == w.channels * w.seqlen
+    assert r["wall_s"] > 0 and r["channel_tokens_per_s"] > 0 and r["GB_s"] > 0
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and h["affinity_cpus"] >= 1 and isinstance(h["cpu_model"], str)
