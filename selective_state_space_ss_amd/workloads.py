@@ -14,7 +14,8 @@ the fixed order x, dt_raw, z, B, C, D, dt_bias, h0/state, reset; draws a
 workload does not use are skipped; ``N(mu, s)`` means ``mu + s * randn``;
 bf16 tensors are the fp32 draws rounded to nearest-even by ``Tensor.to``):
 
-* ``A[c, n] = -(n + 1)`` (S4D-real).
+* ``A[c, n] = -(n + 1)`` (S4D-real); parity cases may instead draw a
+  different A for every (c, n) (``learned_like_A``).
 * ``x, B, C, z, D ~ N(0, 1)``; ``dt_raw ~ N(0, 1)``.
 * ``dt_bias ~ N(-4, 0.5)`` per channel, except ``mamba130m`` where
   ``dt_bias = softplus^-1(u)``, ``u = exp(Uniform(ln 1e-3, ln 0.1))``.
@@ -109,6 +110,18 @@ def s4d_real_A(channels: int, state_dim: int) -> torch.Tensor:
     return row.unsqueeze(0).expand(channels, state_dim).contiguous()
 
 
+def learned_like_A(seed: int, channels: int, state_dim: int) -> torch.Tensor:
+    """A different for every (c, n), as a trained model's A = -exp(A_log)
+    is: ``A = -exp(N(0.5, 1))`` (mostly 0.2 .. 12, tails past 50), with about
+    5 % of the entries exactly 0 (no decay) and 2 % at -5000 (the state
+    forgets within a token). Its own generator, seeded with ``seed``."""
+    gen = torch.Generator().manual_seed(seed)
+    A = -torch.exp(_normal(gen, (channels, state_dim), 0.5, 1.0))
+    u = torch.rand((channels, state_dim), generator=gen)
+    A = torch.where(u < 0.05, torch.zeros_like(A), A)
+    return torch.where((u >= 0.05) & (u < 0.07), torch.full_like(A, -5000.0), A).contiguous()
+
+
 def reset_mask(gen: torch.Generator, batch: int, seqlen: int, mean_doc: int) -> torch.Tensor:
     """uint8 [batch, seqlen]; 1 marks the first token of a document."""
     u = torch.rand((batch, seqlen), generator=gen)
@@ -188,23 +201,33 @@ def algorithmic_bytes(w: Workload) -> int:
 
 def make_case(seed: int, batch: int, channels: int, state_dim: int, seqlen: int, io_dtype: str = "bf16",
               gate: bool = True, h0: bool = True, reset_mean_doc: Optional[int] = None,
-              dt_bias: str = "normal") -> Dict[str, Optional[torch.Tensor]]:
+              dt_bias: str = "normal", a_init: str = "s4d") -> Dict[str, Optional[torch.Tensor]]:
     """An arbitrary-shape prompt case with the workloads' distributions
     (h0 ~ N(0, 0.1) when requested); seqlen == 0 is allowed. Same key set as
-    make_inputs."""
+    make_inputs. a_init="learned" replaces the S4D-real A by
+    learned_like_A(seed + 7919, ...)."""
     w = Workload("case", batch, channels, state_dim, max(seqlen, 1), io_dtype, gate, 0.1 if h0 else None,
                  reset_mean_doc, dt_bias, seed, "parity case")
     out = make_inputs(w, seqlen=seqlen)
+    if a_init == "learned":
+        out["A"] = learned_like_A(seed + 7919, channels, state_dim)
+    elif a_init != "s4d":
+        raise ValueError(f"a_init: {a_init!r}")
     return out
 
 
 def make_decode_case(seed: int, batch: int, channels: int, state_dim: int, io_dtype: str = "bf16",
-                     gate: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+                     gate: bool = True, a_init: str = "s4d") -> Dict[str, Optional[torch.Tensor]]:
     """An arbitrary-shape decode-step case with the decode workload's
-    distributions."""
+    distributions (a_init as for make_case)."""
     w = Workload("decode_case", batch, channels, state_dim, 0, io_dtype, gate, 1.0, None, "normal", seed,
                  "decode parity case")
-    return make_inputs(w)
+    out = make_inputs(w)
+    if a_init == "learned":
+        out["A"] = learned_like_A(seed + 7919, channels, state_dim)
+    elif a_init != "s4d":
+        raise ValueError(f"a_init: {a_init!r}")
+    return out
 
 
 def make_gated_case(seed: int, batch: int, seqlen: int, dk: int, dv: int, io_dtype: str = "bf16",

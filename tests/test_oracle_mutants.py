@@ -33,6 +33,8 @@ MUTANTS = {
                                "h[n] = reset ? 0.0 : a * h[n] + d * Bt[n * bc_stride] * xv;"),
     "reset_ignored": ("double a = reset ? 0.0 : exp(d * A_row[n]);", "double a = exp(d * A_row[n]);"),
     "A_wrong_index": ("exp(d * A_row[n])", "exp(d * A_row[0])"),
+    "A_of_channel_0": ("s6_token(N, h, d, x[i], A + c * N,", "s6_token(N, h, d, x[i], A,"),
+    "decode_A_of_channel_0": ("s6_token(N, state + r * N, d, x[r], A + c * N,", "s6_token(N, state + r * N, d, x[r], A,"),
     "h0_ignored": ("h[n] = h0 ? h0[r * N + n] : 0.0;", "h[n] = 0.0;"),
     "silu_is_sigmoid": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "decode_no_skip": ("yt += (D ? D[c] : 0.0) * x[r];", "yt += 0.0;"),
