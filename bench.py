@@ -548,45 +548,75 @@ FLUSH_BYTES = 1 << 30
 PCT_REPS = 50   # launches behind each configuration's p10 / median / p90
 
 
-def time_cold(f, stream, reps: int, flush) -> float:
+def _event_pairs(n: int, stream):
+    """n pairs of timing events, each recorded once (torch creates an event at
+    its first record) so that its raw handle exists."""
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in pairs:
+        e0.record(stream)
+        e1.record(stream)
+    return pairs
+
+
+def _timed_launches(f, stream, reps: int, before=None, kernel_timed: bool = False):
+    """Per-launch microseconds of `reps` launches of f, each with an event
+    pair around the call; with kernel_timed, f(kev) also passes a second pair
+    (raw handles) that the kernel's own dispatch records, and those durations
+    are returned first. Returns (kernel or call times, call times)."""
+    import torch
+    call = _event_pairs(reps, stream)
+    kern = _event_pairs(reps, stream) if kernel_timed else None
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(call):
+        if before is not None:
+            before()
+        e0.record(stream)
+        if kernel_timed:
+            f((kern[i][0].cuda_event, kern[i][1].cuda_event))
+        else:
+            f()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in call]
+    if kernel_timed:
+        return [k0.elapsed_time(k1) * 1e3 for k0, k1 in kern], call_us
+    return call_us, call_us
+
+
+def time_cold(f, stream, reps: int, flush, kernel_timed: bool = False) -> float:
     """Average microseconds of f when the caches hold none of its data: before
     each timed launch a read of the 1 GiB `flush` tensor (a sum) streams
     through the L2s and the 256 MB last-level cache, leaving them full of
     clean lines (outside the timed region; HIP events on `stream` bracket f
-    alone). A read rather than a fill: written lines would still be draining
-    to HBM while f runs."""
+    alone, and with kernel_timed the kernel's own dispatch records a second
+    pair: f(kev)). A read rather than a fill: written lines would still be
+    draining to HBM while f runs."""
     import torch
     t0 = time.time()
     while time.time() - t0 < EXTRA_WARM_S:
-        f()
+        f(None) if kernel_timed else f()
         torch.cuda.synchronize()
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in pairs:
-        flush.sum()
-        e0.record(stream)
-        f()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    each = [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+    each, call = _timed_launches(f, stream, reps, before=lambda: flush.sum(), kernel_timed=kernel_timed)
     LAST_EACH[:] = each
+    LAST_CALL[:] = call
     return sum(each) / reps
 
 
-# per-launch microseconds of the last time_cold / time_each call
+# per-launch microseconds of the last time_cold / time_each call (the
+# kernel's own duration where it was timed so, else the call's), and of the
+# calls themselves
 LAST_EACH: list = []
+LAST_CALL: list = []
 
 
-def time_each(f, stream, reps: int) -> list:
+def time_each(f, stream, reps: int, kernel_timed: bool = False) -> list:
     """Microseconds of each of `reps` back-to-back launches of f (an event pair
-    around every launch; the caches keep what the previous launch left)."""
-    import torch
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in pairs:
-        e0.record(stream)
-        f()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs]
+    around every launch, and with kernel_timed the pair the kernel's dispatch
+    records; the caches keep what the previous launch left)."""
+    each, call = _timed_launches(f, stream, reps, kernel_timed=kernel_timed)
+    LAST_CALL[:] = call
+    return each
 
 
 def percentiles(each: list) -> dict:
@@ -604,7 +634,11 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
     back to back after a warm-up (warm: the inputs of a small case stay in
     the 256 MB last-level cache between launches) and with the caches flushed
     before every launch (cold). Each also carries p10 / median / p90 of 50
-    launches timed one by one (an event pair around every launch)."""
+    launches timed one by one: the kernel's duration, from the event pair its
+    own dispatch records, and as `median_call_us` the median of an event pair
+    around each call (the dispatch gap included). Cold `us` is the mean
+    kernel duration of those 50 launches; warm `us` is the average over 20
+    back-to-back launches between two events."""
     import torch
     from selective_state_space_ss_amd.workloads import WORKLOADS, make_inputs
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -617,13 +651,15 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
             d = {k: (None if v is None else v.cuda()) for k, v in make_inputs(w).items()}
         y = torch.empty_like(d["x"])
         h = torch.empty(w.batch, w.channels, w.state_dim, dtype=torch.float32, device="cuda")
-        f = lambda d=d, y=y, h=h: ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                                                 dt_bias=d["dt_bias"], h0=d["h0"], reset=d["reset"], y=y,
-                                                 h_last=h)
+        f = lambda kev=None, d=d, y=y, h=h: ss.ss_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"],
+                                                           z=d["z"], dt_bias=d["dt_bias"], h0=d["h0"],
+                                                           reset=d["reset"], y=y, h_last=h, timing_events=kev)
         warm = scan_roofline(w, time_launches(f, stream, reps), rates)
-        warm.update(percentiles(time_each(f, stream, PCT_REPS)))
-        cold = scan_roofline(w, time_cold(f, stream, PCT_REPS, flush), rates)
+        warm.update(percentiles(time_each(f, stream, PCT_REPS, kernel_timed=True)))
+        warm["median_call_us"] = percentiles(LAST_CALL)["median_us"]
+        cold = scan_roofline(w, time_cold(f, stream, PCT_REPS, flush, kernel_timed=True), rates)
         cold.update(percentiles(LAST_EACH))
+        cold["median_call_us"] = percentiles(LAST_CALL)["median_us"]
         res[name] = {"shape": {"batch": w.batch, "channels": w.channels, "state_dim": w.state_dim,
                                "seq": w.seqlen, "io": w.io_dtype, "gate": w.gate, "h0": w.h0 is not None,
                                "reset": w.reset_mean_doc is not None},
@@ -631,14 +667,16 @@ def measure_workloads(ss, stream, rates, P, wp, Dd, wd, reps: int = 20):
         del d, y, h
     state = Dd["state"].clone()
     yd = torch.empty_like(Dd["x"])
-    fd = lambda: ss.ss_state_update(state, Dd["x"], Dd["dt"], Dd["A"], Dd["B"], Dd["C"], D=Dd["D"], z=Dd["z"],
-                                    dt_bias=Dd["dt_bias"], y=yd)
+    fd = lambda kev=None: ss.ss_state_update(state, Dd["x"], Dd["dt"], Dd["A"], Dd["B"], Dd["C"], D=Dd["D"],
+                                             z=Dd["z"], dt_bias=Dd["dt_bias"], y=yd, timing_events=kev)
     res["decode"] = {"shape": {"batch": wd.batch, "channels": wd.channels, "state_dim": wd.state_dim,
                                "io": wd.io_dtype, "gate": wd.gate},
                      "warm": decode_roofline(wd, time_launches(fd, stream, reps)),
-                     "cold": decode_roofline(wd, time_cold(fd, stream, PCT_REPS, flush))}
+                     "cold": decode_roofline(wd, time_cold(fd, stream, PCT_REPS, flush, kernel_timed=True))}
     res["decode"]["cold"].update(percentiles(LAST_EACH))
-    res["decode"]["warm"].update(percentiles(time_each(fd, stream, PCT_REPS)))
+    res["decode"]["cold"]["median_call_us"] = percentiles(LAST_CALL)["median_us"]
+    res["decode"]["warm"].update(percentiles(time_each(fd, stream, PCT_REPS, kernel_timed=True)))
+    res["decode"]["warm"]["median_call_us"] = percentiles(LAST_CALL)["median_us"]
     # The achievable rate of the decode's access pattern on this machine: an
     # in-place read-modify-write of a tensor of the state's size (torch's own
     # elementwise kernel), timed the same two ways.
@@ -974,15 +1012,20 @@ def main():
     state = Dd["state"]
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step(ev=None, kev=None):
+        # ev: three events recorded on the stream around the two calls (a
+        # call's time then includes the dispatch gap before its kernel); kev:
+        # raw handles of two event pairs that the kernels' own dispatches
+        # record (ss_scan_fwd_timed / ss_state_update_timed: the kernel's
+        # duration, what a kernel trace reports)
         if ev is not None:
             ev[0].record(stream)
         ss.ss_scan_fwd(P["x"], P["dt"], P["A"], P["B"], P["C"], D=P["D"], z=P["z"], dt_bias=P["dt_bias"],
-                       h0=P["h0"], y=y, h_last=h_last)
+                       h0=P["h0"], y=y, h_last=h_last, timing_events=None if kev is None else kev[0:2])
         if ev is not None:
             ev[1].record(stream)
         ss.ss_state_update(state, Dd["x"], Dd["dt"], Dd["A"], Dd["B"], Dd["C"], D=Dd["D"], z=Dd["z"],
-                           dt_bias=Dd["dt_bias"], y=yd)
+                           dt_bias=Dd["dt_bias"], y=yd, timing_events=None if kev is None else kev[2:4])
         if ev is not None:
             ev[2].record(stream)
 
@@ -1028,22 +1071,43 @@ def main():
             step()
         torch.cuda.synchronize()
     warm_s = time.perf_counter() - t_w
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed steps: each kernel's duration from the event pair its own
+    # dispatch records. (torch creates an event at its first record, so each
+    # is recorded once on the stream before its raw handle is taken.)
+    kevents = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ks in kevents:
+        for e in ks:
+            e.record(stream)
+    handles = [[e.cuda_event for e in ks] for ks in kevents]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(kev=handles[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    scan_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    upd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    scan_ms = sum(k[0].elapsed_time(k[1]) for k in kevents) / args.steps
+    upd_ms = sum(k[2].elapsed_time(k[3]) for k in kevents) / args.steps
     ms_step = wall * 1e3 / args.steps
+    # The same steps timed per call, with events recorded on the stream around
+    # each call (the dispatch gap included), for comparison
+    n_call = min(args.steps, 50)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_call)]
+    for i in range(n_call):
+        step(events[i])
+    torch.cuda.synchronize()
+    scan_call_ms = sum(e[0].elapsed_time(e[1]) for e in events) / n_call
+    upd_call_ms = sum(e[1].elapsed_time(e[2]) for e in events) / n_call
 
     bytes_p, bytes_d = algorithmic_bytes(wp), algorithmic_bytes(wd)
     ct_p, ct_d = wp.channel_tokens, wd.channel_tokens
     rates = issue_rates()
     scan_r = scan_roofline(wp, scan_ms * 1e3, rates)
     dec_r = decode_roofline(wd, upd_ms * 1e3)
+    for r, call_ms in ((scan_r, scan_call_ms), (dec_r, upd_call_ms)):
+        r["us_call"] = round(call_ms * 1e3, 2)
+        r["timing"] = ("us: the kernel's duration, from events its own dispatch records in each timed step; "
+                       "us_call: events recorded on the stream around the call in 50 more steps (adds the "
+                       "dispatch gap before the kernel)")
     wk = scan_work(wp)
     out = {
         "metric": "selective-scan GB/s + channel-tokens/s at Mamba-2.8B layer shape; % roofline",

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 8
+#define SS_ABI_VERSION 9
 #define SS_MAX_STATE_DIM 64
 #define SS_MAX_GATED_DK 256
 #define SS_MAX_CONV_WIDTH 8
@@ -192,6 +192,24 @@ ss_status ss_scan_fwd_conv(const ss_scan_args* args, const float* conv_w, const 
  * (SS_ERR_NULL). batch == 0 or channels == 0 is a no-op returning SS_OK.
  */
 ss_status ss_state_update(const ss_update_args* args, void* stream);
+
+/*
+ * For measurement: ss_scan_fwd and ss_state_update with a pair of events
+ * that the kernel's own dispatch records, start_event when the kernel starts
+ * and stop_event when it ends, so that hipEventElapsedTime(start, stop) is
+ * the kernel's duration (what a kernel trace reports). An event pair recorded
+ * around the call instead also counts the dispatch gap before the kernel
+ * (about 1.5 to 3 us on MI355X).
+ *
+ *   start_event, stop_event : hipEvent_t created by the caller (with timing
+ *                 enabled), or NULL (then not recorded); owned by the caller.
+ *
+ * Everything else is the untimed call's: arguments, outputs, conventions and
+ * errors. A call that launches nothing (a zero size) records the events on
+ * the stream; a call that returns an error records neither.
+ */
+ss_status ss_scan_fwd_timed(const ss_scan_args* args, void* stream, void* start_event, void* stop_event);
+ss_status ss_state_update_timed(const ss_update_args* args, void* stream, void* start_event, void* stop_event);
 
 /*
  * Scalar-gated state scan ("Mamba 2 Gated State Scan" problem page,

@@ -75,6 +75,10 @@ def load_library() -> ctypes.CDLL:
     lib.ss_dt_proj.argtypes = [i64, i64, i64, i64, i32, vp, vp, vp, i32, vp, vp]
     lib.ss_state_update.restype = i32
     lib.ss_state_update.argtypes = [ctypes.POINTER(UpdateArgs), vp]
+    lib.ss_scan_fwd_timed.restype = i32
+    lib.ss_scan_fwd_timed.argtypes = [ctypes.POINTER(ScanArgs), vp, vp, vp]
+    lib.ss_state_update_timed.restype = i32
+    lib.ss_state_update_timed.argtypes = [ctypes.POINTER(UpdateArgs), vp, vp, vp]
     lib.ss_status_str.restype = ctypes.c_char_p
     lib.ss_status_str.argtypes = [i32]
     lib.ss_abi_version.restype = i32
@@ -122,7 +126,7 @@ def _stream_handle(device, stream) -> Optional[int]:
 
 
 def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=None, dt_softplus: bool = True,
-                *, y=None, h_last=None, return_last_state: bool = True, stream=None) -> Tuple:
+                *, y=None, h_last=None, return_last_state: bool = True, stream=None, timing_events=None) -> Tuple:
     """Prompt scan on the GPU.
 
     x, dt, z: [batch, channels, seq]; B, C: [batch, state_dim, seq] (float32 or
@@ -132,10 +136,16 @@ def ss_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, reset=Non
     float32. Returns (y, h_last); h_last is None when return_last_state is
     False. Preallocated outputs may be passed as y= and h_last= (h_last may be
     h0 itself). Runs on the current torch stream unless stream= is given.
+    timing_events=(start, stop), raw hipEvent_t handles, calls
+    ss_scan_fwd_timed: the kernel's dispatch records them.
     """
     y, h_last, args, dev = _scan_args(x, dt, A, B, C, D, z, dt_bias, h0, reset, dt_softplus, y, h_last,
                                       return_last_state)
-    rc = load_library().ss_scan_fwd(ctypes.byref(args), _stream_handle(dev, stream))
+    lib = load_library()
+    if timing_events is None:
+        rc = lib.ss_scan_fwd(ctypes.byref(args), _stream_handle(dev, stream))
+    else:
+        rc = lib.ss_scan_fwd_timed(ctypes.byref(args), _stream_handle(dev, stream), *timing_events)
     if rc != SS_OK:
         raise SSError(rc, "ss_scan_fwd")
     return y, h_last
@@ -404,10 +414,12 @@ def ss_dt_proj(w_dt, delta, dt_bias=None, *, apply_softplus: bool = False, out=N
 
 
 def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True, *, y=None,
-                    stream=None):
+                    stream=None, timing_events=None):
     """Single-token decode step on the GPU; `state` ([batch, channels,
     state_dim] float32) is updated in place. x, dt, z: [batch, channels];
-    B, C: [batch, state_dim]. Returns y [batch, channels]."""
+    B, C: [batch, state_dim]. Returns y [batch, channels].
+    timing_events=(start, stop), raw hipEvent_t handles, calls
+    ss_state_update_timed: the kernel's dispatch records them."""
     import torch
     if state.dim() != 3:
         raise ValueError("state must be [batch, channels, state_dim]")
@@ -437,7 +449,10 @@ def ss_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_soft
     args = UpdateArgs(batch=batch, channels=channels, state_dim=N, io_dtype=code, state=_ptr(state), x=_ptr(x),
                       dt=_ptr(dt), z=_ptr(z), B=_ptr(B), C=_ptr(C), A=_ptr(A), D=_ptr(D), dt_bias=_ptr(dt_bias),
                       dt_softplus=int(bool(dt_softplus)), y=_ptr(y))
-    rc = lib.ss_state_update(ctypes.byref(args), _stream_handle(dev, stream))
+    if timing_events is None:
+        rc = lib.ss_state_update(ctypes.byref(args), _stream_handle(dev, stream))
+    else:
+        rc = lib.ss_state_update_timed(ctypes.byref(args), _stream_handle(dev, stream), *timing_events)
     if rc != SS_OK:
         raise SSError(rc, "ss_state_update")
     return y

@@ -393,7 +393,7 @@ hipError_t launch_tiles(AttnParams p, hipStream_t stream) {
   void* args[] = {&p};
   const void* fn = p.L <= 256 ? reinterpret_cast<const void*>(&effective_attention_tiles_kernel<IoT, 256>)
                               : reinterpret_cast<const void*>(&effective_attention_tiles_kernel<IoT, 512>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kTW), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(64 * kTW), args, stream);
 }
 
 template <typename IoT, bool PER_STATE>
@@ -410,7 +410,7 @@ hipError_t launch_ps(const AttnParams& p0, hipStream_t stream) {
   else if (p.N <= 16) fn = reinterpret_cast<const void*>(&effective_attention_kernel<IoT, 16, PER_STATE>);
   else if (p.N <= 32) fn = reinterpret_cast<const void*>(&effective_attention_kernel<IoT, 32, PER_STATE>);
   else fn = reinterpret_cast<const void*>(&effective_attention_kernel<IoT, 64, PER_STATE>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, stream);
 }
 
 template <typename IoT>

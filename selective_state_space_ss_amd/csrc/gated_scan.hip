@@ -511,7 +511,7 @@ hipError_t launch_rt(const GatedParams& p0, hipStream_t stream) {
   void* args[] = {&p};
   const void* fn = vec ? reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, true>)
                        : reinterpret_cast<const void*>(&gated_scan_kernel<IoT, StT, RT, false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, stream);
 }
 
 template <typename IoT, typename StT>

@@ -484,7 +484,7 @@ hipError_t launch_tile(const ProjParams& p, hipStream_t stream) {
   void* args[] = {const_cast<ProjParams*>(&p)};
   const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_tile_kernel<IoT, KCH, true>)
                            : reinterpret_cast<const void*>(&dt_proj_tile_kernel<IoT, KCH, false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kProjWaves), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(64 * kProjWaves), args, stream);
 }
 
 template <typename IoT>
@@ -508,7 +508,7 @@ hipError_t launch_conv_io(const ConvParams& p, hipStream_t stream) {
     else fn = reset ? reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 8, true>)
                     : reinterpret_cast<const void*>(&conv1d_silu_kernel<IoT, false, 8, false>);
   }
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kConvThreads), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(kConvThreads), args, stream);
 }
 
 template <typename IoT, bool VEC>
@@ -518,7 +518,7 @@ hipError_t launch_proj_vec(const ProjParams& p, hipStream_t stream) {
   void* args[] = {const_cast<ProjParams*>(&p)};
   const void* fn = p.apply ? reinterpret_cast<const void*>(&dt_proj_kernel<IoT, VEC, true>)
                            : reinterpret_cast<const void*>(&dt_proj_kernel<IoT, VEC, false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kProjThreads), args, 0, stream);
+  return launch_kernel(fn, dim3((unsigned)blocks), dim3(kProjThreads), args, stream);
 }
 
 template <typename IoT>

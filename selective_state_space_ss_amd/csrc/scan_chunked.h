@@ -595,9 +595,8 @@ hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
   const int64_t blocks = p.batch * p.chan_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {&p};
-  return hipLaunchKernel(
-      reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES, CW, RL>),
-      dim3((unsigned)blocks), dim3(S::kThreads), args, 0, stream);
+  return launch_kernel(reinterpret_cast<const void*>(&scan_fwd_kernel<IoT, K, W, NMAX, GATE, RESET, STATES, CW, RL>),
+      dim3((unsigned)blocks), dim3(S::kThreads), args, stream);
 }
 
 // Block shapes. K = 16 tokens per lane keeps a lane's arrays small enough for

@@ -389,8 +389,8 @@ hipError_t launch_t(const ScanParams& p0, hipStream_t stream) {
   const int64_t blocks = p.batch * p.chan_blocks;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&scan_rows_kernel<IoT, GATE, RESET>), dim3((unsigned)blocks),
-                         dim3(kThreads), args, 0, stream);
+  return launch_kernel(reinterpret_cast<const void*>(&scan_rows_kernel<IoT, GATE, RESET>), dim3((unsigned)blocks),
+                       dim3(kThreads), args, stream);
 }
 
 template <typename IoT>

@@ -1,13 +1,52 @@
 // C ABI entry points: validate, pick the kernel instantiation, enqueue.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "ss_scan.h"
 #include "ss_launch.h"
 #include "ss_validate.h"
 
+namespace ss {
+
+TimedLaunch& timed_launch() {
+  static thread_local TimedLaunch t;
+  return t;
+}
+
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream) {
+  TimedLaunch& t = timed_launch();
+  if (t.start || t.stop) {
+    ++t.launches;
+    return hipExtLaunchKernel(fn, grid, block, args, 0, stream, t.start, t.stop, 0);
+  }
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+}  // namespace ss
+
 namespace {
 
 bool vec16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Runs one entry point with the calling thread's event pair set, so that its
+// kernel's dispatch records them (launch_kernel). A call that launches
+// nothing (an empty shape) records them on the stream instead, so that they
+// still mark the call's place; a call that fails leaves them unrecorded.
+template <typename F>
+ss_status timed_call(F&& call, void* stream, void* start, void* stop) {
+  ss::TimedLaunch& t = ss::timed_launch();
+  t = ss::TimedLaunch{static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop), 0};
+  const ss_status st = call();
+  const int launched = t.launches;
+  t = ss::TimedLaunch{};
+  if (st == SS_OK && launched == 0) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((start && hipEventRecord(static_cast<hipEvent_t>(start), s) != hipSuccess) ||
+        (stop && hipEventRecord(static_cast<hipEvent_t>(stop), s) != hipSuccess))
+      return SS_ERR_HIP;
+  }
+  return st;
+}
 
 struct ConvArgs {
   const float* w;
@@ -116,6 +155,14 @@ ss_status ss_state_update(const ss_update_args* args, void* stream) {
   p.y = a.y;
   const hipError_t e = ss::launch_state_update(p, a.io_dtype == SS_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+ss_status ss_scan_fwd_timed(const ss_scan_args* args, void* stream, void* start_event, void* stop_event) {
+  return timed_call([&] { return ss_scan_fwd(args, stream); }, stream, start_event, stop_event);
+}
+
+ss_status ss_state_update_timed(const ss_update_args* args, void* stream, void* start_event, void* stop_event) {
+  return timed_call([&] { return ss_state_update(args, stream); }, stream, start_event, stop_event);
 }
 
 int ss_gated_scan(int64_t batch, int64_t seqlen, int64_t dk, int64_t dv, int io_dtype, int state_dtype,

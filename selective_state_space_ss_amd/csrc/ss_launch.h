@@ -132,6 +132,18 @@ hipError_t launch_gated_scan(const GatedParams& p, bool io_bf16, bool state_bf16
 }  // namespace ss
 
 namespace ss {
+// Every kernel of the library is launched through launch_kernel (no dynamic
+// LDS). A call made through ss_scan_fwd_timed or ss_state_update_timed first
+// sets the calling thread's event pair; launch_kernel then gives the events
+// to the dispatch itself (hipExtLaunchKernel), which records them when the
+// kernel starts and when it ends, and counts the launch.
+struct TimedLaunch {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int launches = 0;
+};
+TimedLaunch& timed_launch();  // the calling thread's
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream);
+
 // Launch-geometry limits, checked by the C ABI before launching.
 int64_t scan_fwd_blocks(int64_t batch, int64_t channels);
 bool state_update_grid_ok(int64_t batch, int64_t channels, int64_t state_dim);

@@ -151,8 +151,8 @@ hipError_t launch_t(const UpdateParams& p, hipStream_t stream) {
   UpdateParams q = p;
   void* args[] = {&q};
   const dim3 grid((unsigned)((p.channels + kThreads / 4 - 1) / (kThreads / 4)), (unsigned)((p.batch + R - 1) / R));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&state_update_kernel<IoT, G, GATE, VEC>), grid,
-                         dim3(kThreads), args, 0, stream);
+  return launch_kernel(reinterpret_cast<const void*>(&state_update_kernel<IoT, G, GATE, VEC>), grid,
+                       dim3(kThreads), args, stream);
 }
 
 template <typename IoT, int G>

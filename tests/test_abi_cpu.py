@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["ss_abi_version", "ss_conv1d_silu", "ss_dt_proj", "ss_effective_attention",
                                     "ss_gated_scan", "ss_scan_fwd", "ss_scan_fwd_conv", "ss_scan_fwd_states",
-                                    "ss_state_update", "ss_status_str"]
+                                    "ss_scan_fwd_timed", "ss_state_update", "ss_state_update_timed",
+                                    "ss_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert ss.abi_version() == 8
+    assert ss.abi_version() == 9
     for code in range(8):
         assert ss.status_str(code).startswith("SS_")
     assert "unknown" in ss.status_str(99)
@@ -95,6 +96,26 @@ def test_null_argument_structs(lib):
     assert lib.ss_scan_fwd(None, None) == NULL
     assert lib.ss_scan_fwd_states(None, 8 * MB, -1, None) == NULL
     assert lib.ss_state_update(None, None) == NULL
+    assert lib.ss_scan_fwd_timed(None, None, None, None) == NULL
+    assert lib.ss_state_update_timed(None, None, None, None) == NULL
+
+
+def test_timed_calls_validate_as_the_untimed_ones(lib):
+    """The timed entry points run the same validation (events NULL: nothing
+    to record, and no device is touched on these paths)."""
+    def timed_scan(**kw):
+        return lib.ss_scan_fwd_timed(ctypes.byref(scan_args(**kw)), None, None, None)
+
+    def timed_upd(**kw):
+        a = UpdateArgs(batch=kw.get("batch", 2), channels=8, state_dim=kw.get("N", 16), io_dtype=kw.get("io", 1),
+                       state=kw.get("state", 1 * MB), x=2 * MB, dt=3 * MB, z=None, B=5 * MB, C=6 * MB, A=4 * MB,
+                       D=None, dt_bias=None, dt_softplus=1, y=kw.get("y", 7 * MB))
+        return lib.ss_state_update_timed(ctypes.byref(a), None, None, None)
+
+    for kw in (dict(io=2), dict(batch=-1), dict(N=65), dict(x=None), dict(y=1 * MB), dict(batch=0)):
+        assert timed_scan(**kw) == scan_call(lib, **kw), kw
+    for kw in (dict(io=7), dict(N=65), dict(state=None), dict(y=2 * MB), dict(batch=0)):
+        assert timed_upd(**kw) == upd_call(lib, **kw), kw
 
 
 def test_struct_layout_matches_header(tmp_path):
