@@ -206,7 +206,10 @@ ss_status ss_state_update(const ss_update_args* args, void* stream);
  *
  * Everything else is the untimed call's: arguments, outputs, conventions and
  * errors. A call that launches nothing (a zero size) records the events on
- * the stream; a call that returns an error records neither.
+ * the stream; a call that returns an error records neither. They are meant
+ * for eager timing: stream capture into a HIP graph is supported for the
+ * untimed calls only. The events are set for the calling thread during the
+ * call, so concurrent timed calls from different threads do not mix.
  */
 ss_status ss_scan_fwd_timed(const ss_scan_args* args, void* stream, void* start_event, void* stop_event);
 ss_status ss_state_update_timed(const ss_update_args* args, void* stream, void* start_event, void* stop_event);
